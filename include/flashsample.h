@@ -1,0 +1,155 @@
+/*
+ * flashsample.h - C ABI of the MI355X (gfx950) fused LM-head sampler.
+ *
+ * Operation (FlashSampling: Fast and Memory-Efficient Exact Sampling,
+ * arXiv 2603.15854, Section 3): given hidden states H [B, D] and LM-head
+ * weights W [V, D], draw one token per batch row from softmax(H W^T / T)
+ * by the Gumbel-max trick,
+ *
+ *     token[b] = argmax_v ( l[b, v] / T + g(seed, step, b, v) ),  l = H W^T,
+ *
+ * where g is standard Gumbel noise that depends only on (seed, step, row b,
+ * vocab index v). The fused entry point computes l tile by tile on chip,
+ * keeps one candidate per (row, vocab tile) (Stage 1 of the method section)
+ * and reduces the candidates to one token per row (Stage 2), so the [B, V]
+ * logits never reach device memory. The unfused entry point is the
+ * two-step baseline of the same section's IO model: a GEMM that writes the
+ * logits, then a sampler that reads them.
+ *
+ * Noise (the pages ask for i.i.d. Gumbels; the generator is this library's
+ * choice): Philox4x32-10 (Salmon et al., SC'11) with key
+ * (seed mod 2^32, seed >> 32) and counter (v >> 2, b, step mod 2^32,
+ * step >> 32); word v & 3 of the output is x, u = (x + 1/2) 2^-32 and
+ * g = -ln(-ln u). Ties go to the lowest vocab index; NaN scores never win;
+ * a row whose scores are all NaN yields -1. T == 0 is greedy argmax of l.
+ *
+ * Conventions for every entry point below:
+ *  - H, W, workspace and outputs are DEVICE pointers owned by the caller;
+ *    the library allocates nothing and keeps no mutable global state.
+ *  - H is row-major [B, D] with row stride ldh elements, W row-major [V, D]
+ *    with row stride ldw elements (ld >= D). Both have the same dtype.
+ *    Base pointers must be 16-byte aligned and ld * sizeof(dtype) and
+ *    D * sizeof(dtype) multiples of 16 (else FS_ERR_UNSUPPORTED).
+ *  - Calls are asynchronous on `stream`: they validate, enqueue and return.
+ *    Only the workspace and the outputs are written. Distinct calls may run
+ *    concurrently if they use distinct workspaces and outputs.
+ *  - Validation is synchronous; on any error nothing is enqueued.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef FLASHSAMPLE_H
+#define FLASHSAMPLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fs_status {
+  FS_OK = 0,
+  FS_ERR_INVALID_ARGUMENT = 1,   /* null pointer, size <= 0 or too large, ld < D, bad T */
+  FS_ERR_UNSUPPORTED = 2,        /* dtype, alignment or option not supported */
+  FS_ERR_WORKSPACE_TOO_SMALL = 3,
+  FS_ERR_HIP = 4                 /* a HIP launch failed; see fs_last_hip_error() */
+} fs_status_t;
+
+typedef enum fs_dtype { FS_DTYPE_BF16 = 0, FS_DTYPE_F32 = 1 } fs_dtype_t;
+
+/* Stage-1 kernel family. AUTO picks by dtype and batch size. */
+typedef enum fs_variant { FS_VARIANT_AUTO = 0, FS_VARIANT_GEMV = 1, FS_VARIANT_MFMA = 2 } fs_variant_t;
+
+/* Options for the _ex entry points; a zero-initialised struct means defaults.
+ * Results never depend on variant or vocab_tile (the argmax decomposes over
+ * any vocab partition), only speed does. */
+typedef struct fs_options {
+  int32_t variant;         /* fs_variant_t */
+  int32_t vocab_tile;      /* rows per Stage-1 vocab tile; 0 = variant default.
+                              Must be a multiple of the variant's granule
+                              (fs_vocab_tile_granule). */
+  void* logits;            /* non-null: the fused call also stores l = H W^T
+                              (device [B, V] row-major, stride ld_logits) */
+  int64_t ld_logits;
+  int32_t logits_dtype;    /* fs_dtype_t of the stored logits */
+  int32_t reserved;
+  hipEvent_t stage1_start; /* non-null: recorded on `stream` right before and */
+  hipEvent_t stage1_stop;  /* right after the Stage-1 launch (for timing) */
+} fs_options_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* fs_status_string(fs_status_t status);
+
+/* hipError_t of the most recent FS_ERR_HIP returned on the calling thread
+ * (0 if none). */
+int fs_last_hip_error(void);
+
+/* Number of Stage-1 vocab tiles the fused call uses for these sizes (the
+ * candidate buffer is [B, n_tiles] 64-bit keys at the start of the
+ * workspace). Returns -1 for invalid sizes or options. */
+int64_t fs_num_vocab_tiles(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
+                           const fs_options_t* opts);
+
+/* Row granule a vocab_tile option must be a multiple of, for a variant. */
+int32_t fs_vocab_tile_granule(fs_variant_t variant);
+
+/* Workspace bytes fs_sample_fused needs (candidate buffer of the Stage-1
+ * tiles: one 64-bit key per (row, vocab tile)). 0 on invalid sizes. */
+size_t fs_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype);
+size_t fs_workspace_bytes_ex(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
+                             const fs_options_t* opts);
+
+/* Fused sampler (FlashSampling Stage 1 + Stage 2; Section 3, the two-stage
+ * list and the exactness paragraph).
+ *   H, ldh, W, ldw, dtype, B, D, V: as in the conventions above.
+ *   temperature: T >= 0 and finite (T == 0: greedy).
+ *   seed, step: noise key and decode step (see the noise paragraph above).
+ *   workspace: device, >= fs_workspace_bytes(...) bytes, 256-byte aligned.
+ *   out_tokens: device int32 [B].
+ * Errors: FS_ERR_INVALID_ARGUMENT, FS_ERR_UNSUPPORTED,
+ *         FS_ERR_WORKSPACE_TOO_SMALL, FS_ERR_HIP. */
+fs_status_t fs_sample_fused(const void* H, int64_t ldh, const void* W, int64_t ldw,
+                            fs_dtype_t dtype, int64_t B, int64_t D, int64_t V,
+                            float temperature, uint64_t seed, uint64_t step,
+                            void* workspace, size_t workspace_bytes,
+                            int32_t* out_tokens, hipStream_t stream);
+
+/* Same, with options (forced variant or vocab tile, optional logits store
+ * as in the pages' IO-model check, Appendix K, and Stage-1 timing events). */
+fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_t ldw,
+                               fs_dtype_t dtype, int64_t B, int64_t D, int64_t V,
+                               float temperature, uint64_t seed, uint64_t step,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t* out_tokens, hipStream_t stream,
+                               const fs_options_t* opts);
+
+/* Workspace of the unfused baseline: the [B, V] logits in logits_dtype plus
+ * the sampler's partial candidates. 0 on invalid sizes. */
+size_t fs_unfused_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
+                                  fs_dtype_t logits_dtype);
+
+/* Unfused baseline of the IO model (Section 3, "the baseline runs two
+ * steps"): GEMM kernel writes l = H W^T to the workspace in logits_dtype,
+ * then a Gumbel-max sampler kernel reads it back. Same noise, tie and NaN
+ * rules as the fused call; with FS_DTYPE_F32 logits the tokens equal the
+ * fused ones, with FS_DTYPE_BF16 the logits are rounded before noise.
+ * Arguments and errors as fs_sample_fused. */
+fs_status_t fs_sample_unfused(const void* H, int64_t ldh, const void* W, int64_t ldw,
+                              fs_dtype_t dtype, int64_t B, int64_t D, int64_t V,
+                              float temperature, uint64_t seed, uint64_t step,
+                              fs_dtype_t logits_dtype,
+                              void* workspace, size_t workspace_bytes,
+                              int32_t* out_tokens, hipStream_t stream);
+
+/* Test hooks (device buffers): the Philox words the kernels use for
+ * vocab indices v0 .. v0+n-1 of row b, and the fp32 Gumbel map the kernels
+ * apply to arbitrary words. */
+fs_status_t fs_test_philox(uint64_t seed, uint64_t step, int64_t b, int64_t v0, int64_t n,
+                           uint32_t* words_out, hipStream_t stream);
+fs_status_t fs_test_gumbel(const uint32_t* words, int64_t n, float* g_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHSAMPLE_H */

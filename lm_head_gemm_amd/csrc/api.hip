@@ -1,0 +1,263 @@
+// C ABI of libflashsample: argument validation, Stage-1 variant and tile
+// selection, workspace layout and kernel launches. Nothing here allocates
+// device memory; every launch goes on the caller's stream.
+#include <cmath>
+#include <cstring>
+
+#include "fs_common.h"
+
+namespace fs {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxB = 65536;
+constexpr int64_t kMaxV = 0x7FFFFFFF;       // tokens are int32
+constexpr int64_t kMaxD = 1 << 20;
+constexpr int32_t kGemvGranule = 16;        // 4 waves x 4-row groups
+constexpr int32_t kGemvDefaultTile = 64;
+constexpr int32_t kSamplePart = 2048;       // unfused sampler: vocab entries per workgroup
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t dtype_size(fs_dtype_t t) { return t == FS_DTYPE_BF16 ? 2 : 4; }
+
+bool dtype_ok(int t) { return t == FS_DTYPE_BF16 || t == FS_DTYPE_F32; }
+
+bool sizes_ok(int64_t B, int64_t D, int64_t V) {
+  return B > 0 && D > 0 && V > 0 && B <= kMaxB && D <= kMaxD && V <= kMaxV;
+}
+
+fs_status_t fail_hip(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return FS_ERR_HIP;
+}
+
+struct Plan {
+  fs_variant_t variant;
+  int32_t tile;
+  int64_t n_tiles;
+};
+
+// Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
+bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* o, Plan* p,
+               fs_status_t* why) {
+  (void)D;
+  *why = FS_ERR_INVALID_ARGUMENT;
+  int variant = o ? o->variant : FS_VARIANT_AUTO;
+  if (variant != FS_VARIANT_AUTO && variant != FS_VARIANT_GEMV && variant != FS_VARIANT_MFMA) return false;
+  if (variant == FS_VARIANT_AUTO) variant = FS_VARIANT_GEMV;
+  (void)B;
+  if (variant == FS_VARIANT_MFMA) {
+    *why = FS_ERR_UNSUPPORTED;
+    return false;
+  }
+  (void)dtype;
+  int32_t tile = o && o->vocab_tile ? o->vocab_tile : kGemvDefaultTile;
+  if (tile < 0 || tile % kGemvGranule != 0) return false;
+  p->variant = (fs_variant_t)variant;
+  p->tile = tile;
+  p->n_tiles = (V + tile - 1) / tile;
+  if (p->n_tiles > 0x7FFFFFFF) return false;
+  return true;
+}
+
+size_t fused_ws_bytes(int64_t B, const Plan& p) {
+  return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign);
+}
+
+int64_t unfused_ld(int64_t V) { return (V + 7) / 8 * 8; }
+int64_t unfused_parts(int64_t V) { return (V + kSamplePart - 1) / kSamplePart; }
+
+size_t unfused_ws_bytes(int64_t B, int64_t V, fs_dtype_t logits_dtype) {
+  const size_t logits = align_up((size_t)B * unfused_ld(V) * dtype_size(logits_dtype), kAlign);
+  return logits + align_up((size_t)B * unfused_parts(V) * sizeof(uint64_t), kAlign);
+}
+
+NoiseKey noise_key(uint64_t seed, uint64_t step) {
+  return NoiseKey{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)step, (uint32_t)(step >> 32)};
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared validation of the sampling entry points.
+fs_status_t check_common(const void* H, int64_t ldh, const void* W, int64_t ldw, int dtype,
+                         int64_t B, int64_t D, int64_t V, float T, const void* ws,
+                         const int32_t* out) {
+  if (!H || !W || !ws || !out) return FS_ERR_INVALID_ARGUMENT;
+  if (!sizes_ok(B, D, V)) return FS_ERR_INVALID_ARGUMENT;
+  if (ldh < D || ldw < D) return FS_ERR_INVALID_ARGUMENT;
+  if (!(T >= 0.f) || !std::isfinite(T)) return FS_ERR_INVALID_ARGUMENT;
+  if (!dtype_ok(dtype)) return FS_ERR_UNSUPPORTED;
+  const int64_t esz = (int64_t)dtype_size((fs_dtype_t)dtype);
+  if (!aligned16(H) || !aligned16(W) || !aligned16(ws)) return FS_ERR_UNSUPPORTED;
+  if ((D * esz) % 16 || (ldh * esz) % 16 || (ldw * esz) % 16) return FS_ERR_UNSUPPORTED;
+  if (D * esz > 160 * 1024) return FS_ERR_UNSUPPORTED;  // one H row must fit LDS
+  return FS_OK;
+}
+
+Stage1Args stage1_args(const void* H, int64_t ldh, const void* W, int64_t ldw, int64_t B,
+                       int64_t D, int64_t V, float T, uint64_t seed, uint64_t step,
+                       const Plan& p) {
+  Stage1Args a{};
+  a.H = H;
+  a.ldh = ldh;
+  a.W = W;
+  a.ldw = ldw;
+  a.B = (int32_t)B;
+  a.D = (int32_t)D;
+  a.V = (int32_t)V;
+  a.greedy = T == 0.f;
+  a.inv_t = T == 0.f ? 0.f : 1.0f / T;
+  a.nk = noise_key(seed, step);
+  a.vocab_tile = p.tile;
+  a.n_tiles = (int32_t)p.n_tiles;
+  return a;
+}
+
+}  // namespace
+}  // namespace fs
+
+using namespace fs;
+
+extern "C" {
+
+const char* fs_status_string(fs_status_t s) {
+  switch (s) {
+    case FS_OK: return "FS_OK";
+    case FS_ERR_INVALID_ARGUMENT: return "FS_ERR_INVALID_ARGUMENT";
+    case FS_ERR_UNSUPPORTED: return "FS_ERR_UNSUPPORTED";
+    case FS_ERR_WORKSPACE_TOO_SMALL: return "FS_ERR_WORKSPACE_TOO_SMALL";
+    case FS_ERR_HIP: return "FS_ERR_HIP";
+  }
+  return "FS_ERR_UNKNOWN";
+}
+
+int fs_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t fs_vocab_tile_granule(fs_variant_t variant) {
+  switch (variant) {
+    case FS_VARIANT_AUTO:
+    case FS_VARIANT_GEMV: return kGemvGranule;
+    default: return -1;
+  }
+}
+
+int64_t fs_num_vocab_tiles(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* opts) {
+  if (!sizes_ok(B, D, V) || !dtype_ok(dtype)) return -1;
+  Plan p;
+  fs_status_t why;
+  if (!make_plan(B, D, V, dtype, opts, &p, &why)) return -1;
+  return p.n_tiles;
+}
+
+size_t fs_workspace_bytes_ex(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* opts) {
+  if (!sizes_ok(B, D, V) || !dtype_ok(dtype)) return 0;
+  Plan p;
+  fs_status_t why;
+  if (!make_plan(B, D, V, dtype, opts, &p, &why)) return 0;
+  return fused_ws_bytes(B, p);
+}
+
+size_t fs_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype) {
+  return fs_workspace_bytes_ex(B, D, V, dtype, nullptr);
+}
+
+fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype,
+                               int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
+                               uint64_t step, void* workspace, size_t workspace_bytes,
+                               int32_t* out_tokens, hipStream_t stream, const fs_options_t* opts) {
+  fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens);
+  if (st != FS_OK) return st;
+  Plan p;
+  if (!make_plan(B, D, V, dtype, opts, &p, &st)) return st;
+  if (opts && opts->logits) {
+    if (!dtype_ok(opts->logits_dtype)) return FS_ERR_UNSUPPORTED;
+    if (opts->ld_logits < V) return FS_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)opts->logits & 15u) != 0) return FS_ERR_UNSUPPORTED;
+  }
+  if (workspace_bytes < fused_ws_bytes(B, p)) return FS_ERR_WORKSPACE_TOO_SMALL;
+
+  Stage1Args a = stage1_args(H, ldh, W, ldw, B, D, V, temperature, seed, step, p);
+  a.cand = static_cast<uint64_t*>(workspace);
+  if (opts && opts->logits) {
+    a.logits = opts->logits;
+    a.ld_logits = opts->ld_logits;
+    a.logits_bf16 = opts->logits_dtype == FS_DTYPE_BF16;
+  }
+  hipError_t e;
+  if (opts && opts->stage1_start && (e = hipEventRecord(opts->stage1_start, stream)) != hipSuccess)
+    return fail_hip(e);
+  e = launch_stage1_gemv(a, dtype, stream);
+  if (e != hipSuccess) return fail_hip(e);
+  if (opts && opts->stage1_stop && (e = hipEventRecord(opts->stage1_stop, stream)) != hipSuccess)
+    return fail_hip(e);
+  e = launch_stage2(a.cand, a.B, a.n_tiles, out_tokens, stream);
+  if (e != hipSuccess) return fail_hip(e);
+  return FS_OK;
+}
+
+fs_status_t fs_sample_fused(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype,
+                            int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
+                            uint64_t step, void* workspace, size_t workspace_bytes, int32_t* out_tokens,
+                            hipStream_t stream) {
+  return fs_sample_fused_ex(H, ldh, W, ldw, dtype, B, D, V, temperature, seed, step, workspace,
+                            workspace_bytes, out_tokens, stream, nullptr);
+}
+
+size_t fs_unfused_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
+                                  fs_dtype_t logits_dtype) {
+  if (!sizes_ok(B, D, V) || !dtype_ok(dtype) || !dtype_ok(logits_dtype)) return 0;
+  return unfused_ws_bytes(B, V, logits_dtype);
+}
+
+fs_status_t fs_sample_unfused(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype,
+                              int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
+                              uint64_t step, fs_dtype_t logits_dtype, void* workspace,
+                              size_t workspace_bytes, int32_t* out_tokens, hipStream_t stream) {
+  fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens);
+  if (st != FS_OK) return st;
+  if (!dtype_ok(logits_dtype)) return FS_ERR_UNSUPPORTED;
+  if (workspace_bytes < unfused_ws_bytes(B, V, logits_dtype)) return FS_ERR_WORKSPACE_TOO_SMALL;
+
+  Plan p;
+  if (!make_plan(B, D, V, dtype, nullptr, &p, &st)) return st;
+  const int64_t ld = unfused_ld(V);
+  const size_t logits_bytes = align_up((size_t)B * ld * dtype_size(logits_dtype), kAlign);
+  char* ws = static_cast<char*>(workspace);
+  uint64_t* partial = reinterpret_cast<uint64_t*>(ws + logits_bytes);
+  const int32_t n_parts = (int32_t)unfused_parts(V);
+
+  // step 1: GEMM that writes the logits
+  Stage1Args a = stage1_args(H, ldh, W, ldw, B, D, V, temperature, seed, step, p);
+  a.cand = nullptr;
+  a.logits = ws;
+  a.ld_logits = ld;
+  a.logits_bf16 = logits_dtype == FS_DTYPE_BF16;
+  hipError_t e = launch_stage1_gemv(a, dtype, stream);
+  if (e != hipSuccess) return fail_hip(e);
+  // step 2: sampler that reads them back
+  e = launch_sample_logits(ws, ld, a.logits_bf16, a.B, a.V, a.inv_t, a.greedy, a.nk, kSamplePart, n_parts,
+                           partial, stream);
+  if (e != hipSuccess) return fail_hip(e);
+  e = launch_stage2(partial, a.B, n_parts, out_tokens, stream);
+  if (e != hipSuccess) return fail_hip(e);
+  return FS_OK;
+}
+
+fs_status_t fs_test_philox(uint64_t seed, uint64_t step, int64_t b, int64_t v0, int64_t n,
+                           uint32_t* words_out, hipStream_t stream) {
+  if (!words_out || n <= 0 || v0 < 0 || b < 0 || b > 0xFFFFFFFFll || v0 + n > (int64_t)1 << 34)
+    return FS_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_test_philox(noise_key(seed, step), (uint32_t)b, v0, n, words_out, stream);
+  return e == hipSuccess ? FS_OK : fail_hip(e);
+}
+
+fs_status_t fs_test_gumbel(const uint32_t* words, int64_t n, float* g_out, hipStream_t stream) {
+  if (!words || !g_out || n <= 0 || n > ((int64_t)1 << 32)) return FS_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_test_gumbel(words, n, g_out, stream);
+  return e == hipSuccess ? FS_OK : fail_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Internal header shared by the HIP translation units of libflashsample.
+//
+// Device side: the noise (Philox4x32-10 -> uniform -> Gumbel), the packed
+// 64-bit candidate key, and small wavefront helpers. Host side: the launch
+// helper and the declarations of each kernel family's launcher.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+#include "../../include/flashsample.h"
+
+namespace fs {
+
+// ------------------------------------------------------------------ noise
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw: "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11, Section 4): ten rounds of two 32x32->64-bit
+// multiplies with the paper's multipliers, the key bumped by its Weyl
+// constants between rounds.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+struct Key2 {
+  uint32_t k0, k1;
+};
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * c.x;
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+                   (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return c;
+}
+
+// The four words for vocab indices 4q .. 4q+3 of batch row b.
+struct NoiseKey {
+  uint32_t seed_lo, seed_hi, step_lo, step_hi;
+};
+
+__device__ __forceinline__ uint4 philox_quad(const NoiseKey& nk, uint32_t q, uint32_t b) {
+  return philox4x32_10(make_uint4(q, b, nk.step_lo, nk.step_hi), nk.seed_lo, nk.seed_hi);
+}
+
+__device__ __forceinline__ uint32_t pick_word(const uint4& w, int j) {
+  return j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
+}
+
+// Standard Gumbel from a 32-bit word: u = (x + 1/2) 2^-32, g = -ln(-ln u).
+// For u <= 1/2, -ln u is taken directly; for u > 1/2 it is -log1p(-(1 - u))
+// with 1 - u = (~x + 1/2) 2^-32 formed from the integer, so the small
+// argument keeps full relative precision where the largest Gumbels live.
+// Each uniform carries one fp32 rounding (relative 2^-24), which moves g by
+// at most ~1e-7 plus the fp32 rounding of g itself.
+__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
+  float e;
+  if (x < 0x80000000u) {
+    const float u = fmaf((float)x, 0x1p-32f, 0x1p-33f);
+    e = -logf(u);
+  } else {
+    const float c = fmaf((float)(~x), 0x1p-32f, 0x1p-33f);
+    e = -log1pf(-c);
+  }
+  return -logf(e);
+}
+
+// ------------------------------------------------------------------ candidate keys
+// A candidate (score s, vocab index v) packs into one 64-bit key whose
+// unsigned order is (s ascending, v descending):
+//   key = ord(s) << 32 | (0xFFFFFFFF - v),
+// ord() flips float bits into an order-preserving unsigned int. NaN scores
+// and "no candidate" are key 0, which loses to every real candidate, so the
+// maximum key is the highest score with the lowest index on ties.
+__device__ __forceinline__ uint64_t pack_key(float s, uint32_t v) {
+  const uint32_t bits = __float_as_uint(s);
+  const uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+  const uint64_t key = ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - v);
+  return (s != s) ? 0ull : key;
+}
+
+__device__ __forceinline__ int32_t key_to_token(uint64_t key) {
+  return key == 0ull ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
+  const uint32_t lo = __shfl_xor((uint32_t)x, mask);
+  const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ------------------------------------------------------------------ host
+// Launch through hipLaunchKernel so the launch status comes back directly.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                         hipStream_t stream, Args&&... args) {
+  std::tuple<KArgs...> packed(std::forward<Args>(args)...);
+  return std::apply(
+      [&](auto&... a) {
+        void* ptrs[] = {(void*)&a...};
+        return hipLaunchKernel((const void*)kernel, grid, block, ptrs, lds, stream);
+      },
+      packed);
+}
+
+// Parameters common to the Stage-1 kernels.
+struct Stage1Args {
+  const void* H;
+  int64_t ldh;
+  const void* W;
+  int64_t ldw;
+  int32_t B, D, V;
+  float inv_t;          // 1 / T (unused when greedy)
+  int32_t greedy;       // T == 0
+  NoiseKey nk;
+  int32_t vocab_tile;   // rows per tile
+  int32_t n_tiles;
+  uint64_t* cand;       // [B, n_tiles] keys, or null (store-only)
+  void* logits;         // [B, V] logits, or null
+  int64_t ld_logits;
+  int32_t logits_bf16;  // stored logits dtype
+};
+
+// Launchers (each returns the hipError_t of its launches).
+hipError_t launch_stage1_gemv(const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream);
+int gemv_batch_tile(int64_t B, int64_t D, fs_dtype_t dtype);
+hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32_t* out,
+                         hipStream_t stream);
+hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,
+                                int32_t V, float inv_t, int32_t greedy, NoiseKey nk,
+                                int32_t part, int32_t n_parts, uint64_t* partial,
+                                hipStream_t stream);
+hipError_t launch_test_philox(NoiseKey nk, uint32_t b, int64_t v0, int64_t n, uint32_t* out,
+                              hipStream_t stream);
+hipError_t launch_test_gumbel(const uint32_t* words, int64_t n, float* out, hipStream_t stream);
+
+}  // namespace fs

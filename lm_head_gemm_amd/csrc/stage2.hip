@@ -1,0 +1,131 @@
+// Stage 2 of FlashSampling (arXiv 2603.15854, Section 3, "Stage 2
+// (Reduction)"): per batch row, the maximum of the packed candidate keys over
+// the vocab tiles, decoded to a token. Also the unfused baseline's sampler
+// (Gumbel-max over logits read back from device memory; the "sample from the
+// logits" step of the same section's IO model) and the noise test hooks.
+#include "fs_common.h"
+
+namespace fs {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One workgroup per batch row; keys are read with 256 lanes in parallel.
+__global__ __launch_bounds__(kThreads) void stage2_kernel(const uint64_t* __restrict__ cand,
+                                                          int32_t n_tiles,
+                                                          int32_t* __restrict__ out) {
+  __shared__ uint64_t red[kThreads / 64];
+  const int row = blockIdx.x;
+  const uint64_t* c = cand + (int64_t)row * n_tiles;
+  uint64_t best = 0ull;
+  for (int t = threadIdx.x; t < n_tiles; t += kThreads) best = umax64(best, c[t]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t k = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) k = umax64(k, red[w]);
+    out[row] = key_to_token(k);
+  }
+}
+
+// Gumbel-max over materialised logits: workgroup (part, row) scans `part`
+// consecutive vocab entries of one row, four at a time (one Philox call per
+// four), and writes its best key to partial[row, part].
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void sample_logits_kernel(
+    const void* __restrict__ logits, int64_t ld, int32_t V, float inv_t, int32_t greedy,
+    NoiseKey nk, int32_t part, int32_t n_parts, uint64_t* __restrict__ partial) {
+  __shared__ uint64_t red[kThreads / 64];
+  const int row = blockIdx.y;
+  const int v_begin = blockIdx.x * part;
+  const int v_end = min(V, v_begin + part);
+  uint64_t best = 0ull;
+  for (int v0 = v_begin + 4 * threadIdx.x; v0 < v_end; v0 += 4 * kThreads) {
+    float l[4];
+    if (BF16) {
+      const uint16_t* p = static_cast<const uint16_t*>(logits) + (int64_t)row * ld + v0;
+      if (v0 + 3 < v_end) {
+        const uint2 q = *reinterpret_cast<const uint2*>(p);
+        l[0] = bf16_lo(q.x); l[1] = bf16_hi(q.x); l[2] = bf16_lo(q.y); l[3] = bf16_hi(q.y);
+      } else {
+        for (int j = 0; j < 4; ++j) l[j] = v0 + j < v_end ? __uint_as_float((uint32_t)p[j] << 16) : 0.f;
+      }
+    } else {
+      const float* p = static_cast<const float*>(logits) + (int64_t)row * ld + v0;
+      if (v0 + 3 < v_end) {
+        const float4 q = *reinterpret_cast<const float4*>(p);
+        l[0] = q.x; l[1] = q.y; l[2] = q.z; l[3] = q.w;
+      } else {
+        for (int j = 0; j < 4; ++j) l[j] = v0 + j < v_end ? p[j] : 0.f;
+      }
+    }
+    uint4 words = make_uint4(0u, 0u, 0u, 0u);
+    if (!greedy) words = philox_quad(nk, (uint32_t)(v0 >> 2), (uint32_t)row);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float s = greedy ? l[j] : fmaf(l[j], inv_t, gumbel_from_word(pick_word(words, j)));
+      if (v0 + j < v_end) best = umax64(best, pack_key(s, (uint32_t)(v0 + j)));
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t k = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) k = umax64(k, red[w]);
+    partial[(int64_t)row * n_parts + blockIdx.x] = k;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void test_philox_kernel(NoiseKey nk, uint32_t b, int64_t v0,
+                                                               int64_t n, uint32_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const int64_t v = v0 + i;
+  const uint4 w = philox_quad(nk, (uint32_t)(v >> 2), b);
+  out[i] = pick_word(w, (int)(v & 3));
+}
+
+__global__ __launch_bounds__(kThreads) void test_gumbel_kernel(const uint32_t* words, int64_t n,
+                                                               float* out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  out[i] = gumbel_from_word(words[i]);
+}
+
+}  // namespace
+
+hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32_t* out,
+                         hipStream_t stream) {
+  return launch(stage2_kernel, dim3(B), dim3(kThreads), 0, stream, cand, n_tiles, out);
+}
+
+hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,
+                                int32_t V, float inv_t, int32_t greedy, NoiseKey nk,
+                                int32_t part, int32_t n_parts, uint64_t* partial,
+                                hipStream_t stream) {
+  const dim3 grid(n_parts, B);
+  if (logits_bf16)
+    return launch(sample_logits_kernel<true>, grid, dim3(kThreads), 0, stream, logits, ld, V, inv_t,
+                  greedy, nk, part, n_parts, partial);
+  return launch(sample_logits_kernel<false>, grid, dim3(kThreads), 0, stream, logits, ld, V, inv_t,
+                greedy, nk, part, n_parts, partial);
+}
+
+hipError_t launch_test_philox(NoiseKey nk, uint32_t b, int64_t v0, int64_t n, uint32_t* out,
+                              hipStream_t stream) {
+  const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+  return launch(test_philox_kernel, grid, dim3(kThreads), 0, stream, nk, b, v0, n, out);
+}
+
+hipError_t launch_test_gumbel(const uint32_t* words, int64_t n, float* out, hipStream_t stream) {
+  const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+  return launch(test_gumbel_kernel, grid, dim3(kThreads), 0, stream, words, n, out);
+}
+
+}  // namespace fs

@@ -1,0 +1,145 @@
+"""The C ABI library loads, exports every entry point include/*.h declares, and
+rejects invalid arguments synchronously with the documented status codes
+(no device is needed: nothing is launched on a validation error)."""
+import ctypes
+import glob
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "lm_head_gemm_amd", "libflashsample.so")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIP = 0, 1, 2, 3, 4
+BF16, F32 = 0, 1
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(fs_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (python -m lm_head_gemm_amd.build)")
+    from lm_head_gemm_amd import flashsample  # sets argtypes/restypes
+    return flashsample._lib
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("fs_sample_fused", "fs_sample_unfused", "fs_workspace_bytes", "fs_status_string",
+                 "fs_sample_fused_ex", "fs_unfused_workspace_bytes", "fs_last_hip_error"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+
+
+def test_status_strings(lib):
+    assert lib.fs_status_string(OK) == b"FS_OK"
+    assert lib.fs_status_string(WS_SMALL) == b"FS_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.fs_status_string(99) == b"FS_ERR_UNKNOWN"
+    assert lib.fs_last_hip_error() == 0
+
+
+def test_workspace_sizes(lib):
+    from lm_head_gemm_amd.flashsample import FsOptions
+    nt = lib.fs_num_vocab_tiles(1, 4096, 128256, BF16, None)
+    assert nt > 0
+    ws = lib.fs_workspace_bytes(1, 4096, 128256, BF16)
+    assert ws >= 8 * nt and ws % 256 == 0
+    assert lib.fs_workspace_bytes(0, 4096, 128256, BF16) == 0
+    assert lib.fs_workspace_bytes(1, 4096, 2**31, BF16) == 0
+    assert lib.fs_workspace_bytes(1, 4096, 10, 7) == 0
+    o = FsOptions()
+    g = lib.fs_vocab_tile_granule(1)
+    o.vocab_tile = 3 * g
+    assert lib.fs_num_vocab_tiles(2, 64, 1000, BF16, ctypes.byref(o)) == math.ceil(1000 / (3 * g))
+    o.vocab_tile = g + 1
+    assert lib.fs_num_vocab_tiles(2, 64, 1000, BF16, ctypes.byref(o)) == -1
+    assert lib.fs_workspace_bytes_ex(2, 64, 1000, BF16, ctypes.byref(o)) == 0
+    uw = lib.fs_unfused_workspace_bytes(4, 4096, 1000, BF16, F32)
+    assert uw >= 4 * 1000 * 4
+
+
+def _fused(lib, **kw):
+    a = dict(H=FAKE, ldh=64, W=FAKE, ldw=64, dtype=BF16, B=2, D=64, V=1000, T=1.0, seed=0, step=0,
+             ws=FAKE, wsb=1 << 20, out=FAKE, stream=None, opts=None)
+    a.update(kw)
+    args = [a["H"], a["ldh"], a["W"], a["ldw"], a["dtype"], a["B"], a["D"], a["V"], a["T"], a["seed"],
+            a["step"], a["ws"], a["wsb"], a["out"], a["stream"]]
+    if a["opts"] is None:
+        return lib.fs_sample_fused(*args)
+    return lib.fs_sample_fused_ex(*args, ctypes.byref(a["opts"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=None), INVALID), (dict(W=None), INVALID), (dict(ws=None), INVALID), (dict(out=None), INVALID),
+    (dict(B=0), INVALID), (dict(B=-3), INVALID), (dict(D=0), INVALID), (dict(V=0), INVALID),
+    (dict(V=2**31), INVALID), (dict(B=2**20), INVALID),
+    (dict(ldh=32), INVALID), (dict(ldw=63), INVALID),
+    (dict(T=-1.0), INVALID), (dict(T=float("nan")), INVALID), (dict(T=float("inf")), INVALID),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(H=FAKE + 2), UNSUPPORTED), (dict(W=FAKE + 8), UNSUPPORTED), (dict(ws=FAKE + 4), UNSUPPORTED),
+    (dict(D=12, ldh=12, ldw=12), UNSUPPORTED), (dict(ldh=68), UNSUPPORTED),
+    (dict(D=128 * 1024, ldh=128 * 1024, ldw=128 * 1024), UNSUPPORTED),
+    (dict(wsb=8), WS_SMALL),
+])
+def test_fused_validation(lib, kw, status):
+    assert _fused(lib, **kw) == status
+
+
+def test_fused_option_validation(lib):
+    from lm_head_gemm_amd.flashsample import FsOptions
+    o = FsOptions()
+    o.variant = 9
+    assert _fused(lib, opts=o) == INVALID
+    o = FsOptions()
+    o.vocab_tile = 17
+    assert _fused(lib, opts=o) == INVALID
+    o = FsOptions()
+    o.vocab_tile = -16
+    assert _fused(lib, opts=o) == INVALID
+    o = FsOptions()
+    o.logits = FAKE
+    o.ld_logits = 999
+    assert _fused(lib, opts=o) == INVALID
+    o.ld_logits = 1000
+    o.logits_dtype = 5
+    assert _fused(lib, opts=o) == UNSUPPORTED
+    o.logits_dtype = F32
+    o.logits = FAKE + 4
+    assert _fused(lib, opts=o) == UNSUPPORTED
+    o.logits = FAKE
+    assert _fused(lib, opts=o, wsb=0) == WS_SMALL
+
+
+def test_unfused_validation(lib):
+    base = [FAKE, 64, FAKE, 64, BF16, 2, 64, 1000, 1.0, 0, 0]
+    assert lib.fs_sample_unfused(*base, 9, FAKE, 1 << 20, FAKE, None) == UNSUPPORTED
+    assert lib.fs_sample_unfused(*base, F32, FAKE, 16, FAKE, None) == WS_SMALL
+    bad = list(base)
+    bad[0] = None
+    assert lib.fs_sample_unfused(*bad, F32, FAKE, 1 << 20, FAKE, None) == INVALID
+    bad = list(base)
+    bad[8] = -0.5
+    assert lib.fs_sample_unfused(*bad, F32, FAKE, 1 << 20, FAKE, None) == INVALID
+
+
+def test_test_hooks_validation(lib):
+    assert lib.fs_test_philox(0, 0, 0, 0, 0, FAKE, None) == INVALID
+    assert lib.fs_test_philox(0, 0, -1, 0, 4, FAKE, None) == INVALID
+    assert lib.fs_test_philox(0, 0, 0, 0, 4, None, None) == INVALID
+    assert lib.fs_test_gumbel(None, 4, FAKE, None) == INVALID
+    assert lib.fs_test_gumbel(FAKE, 0, FAKE, None) == INVALID

@@ -1,0 +1,237 @@
+"""Parity of the HIP sampler with the CPU oracle (FlashSampling, arXiv
+2603.15854, Section 3), through the C ABI.
+
+Small cases span several vocab tiles, ragged tails, several batch tiles and
+the degenerate cases (V = 1, greedy ties, NaN rows). The full-size workloads
+run at the sizes and launch configuration the benchmark times, with the
+oracle computing a sample of rows one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from lm_head_gemm_amd import inputs
+from tests._util import TOL, check_parity, to_device
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def fs():
+    import torch
+    assert torch.cuda.is_available()
+    from lm_head_gemm_amd import flashsample
+    return flashsample
+
+
+def _rand_head(seed, B, D, V, dtype="bf16", sigma=0.05):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((B, D), dtype=np.float32)
+    w = rng.standard_normal((V, D), dtype=np.float32) * np.float32(sigma)
+    if dtype == "bf16":
+        return inputs.f32_to_bf16_bits(h), inputs.f32_to_bf16_bits(w)
+    return h, w
+
+
+# ------------------------------------------------------------------ tiny fp32 workload
+
+def test_tiny_f32_64_steps_match_golden(fs):
+    wl = inputs.WORKLOADS["tiny_f32"]
+    H, W = inputs.make_hidden(wl), inputs.make_weights(wl)
+    Hd, Wd = to_device(H), to_device(W)
+    want = {}
+    with open(os.path.join(GOLDEN, "tiny_f32_tokens.txt")) as f:
+        for line in f:
+            if not line.startswith("#"):
+                p = line.split()
+                want[int(p[0])] = (int(p[1]), float(p[3]))
+    for tile in (wl.vocab_tile, 0):
+        for step in wl.steps:
+            tok = int(fs.sample_fused(Hd, Wd, wl.temperature, wl.seed, step, vocab_tile=tile).cpu()[0])
+            idx, margin = want[step]
+            if margin > TOL:
+                assert tok == idx, f"step {step} tile {tile}: {tok} != {idx}"
+            else:
+                check_parity(H, W, wl.temperature, wl.seed, step, [0], [tok])
+
+
+# ------------------------------------------------------------------ small shapes
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,D,V", [
+    (1, 64, 1), (1, 64, 5), (1, 256, 1000), (2, 200, 4099), (3, 1032, 3000),
+    (5, 512, 777), (8, 4096, 2053), (13, 264, 1500),
+])
+@pytest.mark.parametrize("T", [1.0, 0.7, 0.0])
+def test_small_shapes(fs, dtype, B, D, V, T):
+    H, W = _rand_head(B * 1000 + D + V, B, D, V, dtype)
+    Hd, Wd = to_device(H), to_device(W)
+    for seed, step in ((0, 0), (12345, 2**32 + 7)):
+        tok = fs.sample_fused(Hd, Wd, T, seed, step).cpu().numpy()
+        check_parity(H, W, T, seed, step, np.arange(B), tok)
+
+
+@pytest.mark.parametrize("tile", [16, 48, 64, 256, 1008, 4096])
+def test_vocab_tile_invariance(fs, tile):
+    B, D, V = 6, 512, 5003
+    H, W = _rand_head(7, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    ref = fs.sample_fused(Hd, Wd, 0.9, 3, 11).cpu().numpy()
+    got = fs.sample_fused(Hd, Wd, 0.9, 3, 11, vocab_tile=tile).cpu().numpy()
+    r = oracle.sample(H, W, 0.9, 3, 11)
+    firm = r.margin > TOL
+    assert np.array_equal(got[firm], ref[firm])
+    check_parity(H, W, 0.9, 3, 11, np.arange(B), got)
+
+
+def test_batch_prefix_and_repeat_determinism(fs):
+    B, D, V = 13, 256, 3001
+    H, W = _rand_head(9, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    full = fs.sample_fused(Hd, Wd, 1.0, 5, 2).cpu().numpy()
+    for b in (1, 4, 8, 9):
+        assert np.array_equal(fs.sample_fused(Hd[:b], Wd, 1.0, 5, 2).cpu().numpy(), full[:b])
+    for _ in range(20):
+        assert np.array_equal(fs.sample_fused(Hd, Wd, 1.0, 5, 2).cpu().numpy(), full)
+
+
+def test_greedy_ties_lowest_index(fs):
+    B, D, V = 3, 64, 999
+    H, W = _rand_head(1, B, D, V)
+    hv = inputs.bf16_bits_to_f32(H)
+    for b, dup in enumerate((17, 500, 998)):
+        W[dup] = inputs.f32_to_bf16_bits(hv[b] * np.float32(0.5))
+        W[dup + 1 if dup + 1 < V else 0] = W[dup]
+    W[0] = W[998]  # tie between 998 and 0: lowest index is 0
+    Hd, Wd = to_device(H), to_device(W)
+    got = fs.sample_fused(Hd, Wd, 0.0, 0, 0).cpu().numpy()
+    want = oracle.sample(H, W, 0.0, 0, 0).idx
+    assert got.tolist() == want.tolist()
+    assert want[2] == 0
+
+
+def test_nan_row_returns_minus_one(fs):
+    B, D, V = 3, 64, 300
+    H, W = _rand_head(2, B, D, V, "f32")
+    H[1, :] = np.nan
+    Hd, Wd = to_device(H), to_device(W)
+    for T in (1.0, 0.0):
+        got = fs.sample_fused(Hd, Wd, T, 1, 1).cpu().numpy()
+        assert got[1] == -1
+        check_parity(H[[0, 2]], W, T, 1, 1, [0], [got[0]])
+        # row 2's noise is keyed by its row index 2
+        r = oracle.sample(H, W, T, 1, 1, rows=[2])
+        assert r.margin[0] <= TOL or got[2] == r.idx[0]
+
+
+def test_out_of_range_noise_keys(fs):
+    """Large seeds and steps whose high words are non-zero."""
+    B, D, V = 4, 128, 2000
+    H, W = _rand_head(3, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    for seed, step in ((2**64 - 1, 2**64 - 1), (2**40 + 3, 2**33)):
+        tok = fs.sample_fused(Hd, Wd, 1.0, seed, step).cpu().numpy()
+        check_parity(H, W, 1.0, seed, step, np.arange(B), tok)
+
+
+# ------------------------------------------------------------------ unfused baseline and logits store
+
+@pytest.mark.parametrize("B,D,V", [(1, 256, 4099), (5, 1032, 3000), (8, 4096, 2053)])
+def test_unfused_f32_logits_parity(fs, B, D, V):
+    import torch
+    H, W = _rand_head(B + D, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    for T in (1.0, 0.0):
+        tok = fs.sample_unfused(Hd, Wd, T, 7, 3, logits_dtype=torch.float32).cpu().numpy()
+        check_parity(H, W, T, 7, 3, np.arange(B), tok)
+        tok16 = fs.sample_unfused(Hd, Wd, T, 7, 3, logits_dtype=torch.bfloat16).cpu().numpy()
+        assert tok16.min() >= 0 and tok16.max() < V
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_store_logits_option(fs, dtype):
+    import torch
+    B, D, V = 5, 520, 2001
+    H, W = _rand_head(4, B, D, V, dtype)
+    Hd, Wd = to_device(H), to_device(W)
+    exact = oracle.exact_logits(H, W)
+    l32 = torch.full((B, V + 3), float("nan"), dtype=torch.float32, device="cuda")
+    tok = fs.sample_fused(Hd, Wd, 1.0, 0, 0, logits=l32[:, :V]).cpu().numpy()
+    got = l32[:, :V].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - exact)) < 1e-4
+    assert np.isnan(l32[:, V:].cpu().numpy()).all()  # nothing written past V
+    check_parity(H, W, 1.0, 0, 0, np.arange(B), tok)
+    l16 = torch.zeros((B, V), dtype=torch.bfloat16, device="cuda")
+    fs.sample_fused(Hd, Wd, 1.0, 0, 0, logits=l16)
+    got16 = l16.float().cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got16 - exact) / np.maximum(np.abs(exact), 1e-3)) < 2 ** -8 + 1e-4
+
+
+# ------------------------------------------------------------------ distribution
+
+def test_chi_square_on_device(fs):
+    """V = 64 head, 10^6 draws (1000 identical rows x 1000 steps): the device
+    reproduces the oracle's draws and passes chi-square against softmax."""
+    import torch
+    from scipy import stats
+    h, w = inputs.chi2_inputs(0)
+    H = np.repeat(h[None, :], 1000, axis=0)
+    Hd, Wd = to_device(H), to_device(w)
+    out = torch.empty((1000, 1000), dtype=torch.int32, device="cuda")
+    for step in range(1000):
+        fs.sample_fused(Hd, Wd, 1.0, 0, step, out=out[step])
+    draws = out.cpu().numpy()
+    mism = 0
+    for step in range(0, 1000, 50):
+        r = oracle.sample(H, w, 1.0, 0, step)
+        firm = r.margin > TOL
+        mism += int(np.sum(draws[step][firm] != r.idx[firm]))
+    assert mism == 0
+    l = oracle.exact_logits(h, w)[0]
+    p = np.exp(l - l.max())
+    p /= p.sum()
+    counts = np.bincount(draws.ravel(), minlength=64)
+    assert stats.chisquare(counts, p * counts.sum()).pvalue > 1e-3
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+FULL = ["llama3_8b", "qwen_7b", "llama3_70b", "deepseek_v3"]
+
+
+@pytest.fixture(scope="module", params=FULL)
+def full_workload(request):
+    wl = inputs.WORKLOADS[request.param]
+    H = inputs.make_hidden(wl)
+    W = inputs.make_weights(wl)
+    return wl, H, W
+
+
+def test_full_size_sampled_rows(fs, full_workload):
+    """Every B of the workload's sweep, in the default launch configuration.
+    H for a smaller B is a prefix of H, and a row's noise is keyed by its
+    index, so one oracle pass over the union of sampled rows serves all B."""
+    wl, H, W = full_workload
+    Hd, Wd = to_device(H), to_device(W)
+    rng = np.random.default_rng(wl.seed)
+    picked = {}
+    for B in wl.batches:
+        tok = fs.sample_fused(Hd[:B], Wd, wl.temperature, wl.seed, 0).cpu().numpy()
+        assert tok.min() >= 0 and tok.max() < wl.V
+        rows = np.unique(np.concatenate([[0, B - 1], rng.choice(B, size=min(B, 6), replace=False)]))
+        picked[B] = (rows, tok[rows])
+    union = np.unique(np.concatenate([r for r, _ in picked.values()]))
+    ref = oracle.sample(H, W, wl.temperature, wl.seed, 0, rows=union)
+    pos = {int(r): k for k, r in enumerate(union)}
+    total = near = 0
+    for B, (rows, tok) in picked.items():
+        sel = [pos[int(r)] for r in rows]
+        sub = oracle.SampleResult(ref.idx[sel], ref.best[sel], ref.second[sel], ref.second_idx[sel])
+        n, k = check_parity(H, W, wl.temperature, wl.seed, 0, rows, tok, ref=sub)
+        total += n
+        near += k
+    print(f"{wl.name}: {total} row checks over B={list(wl.batches)}, near-tie fraction {near / total:.4f}")
