@@ -53,15 +53,16 @@ def stage1_bytes(B, D, V, esz, n_tiles) -> int:
     return V * D * esz + B * D * esz + 8 * B * n_tiles
 
 
-def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto"):
+def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0):
     """Returns (ms per step, mean Stage-1 ms) over `steps` timed calls."""
     import torch
     T, seed = wl.temperature, wl.seed
-    ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, variant=variant), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, variant=variant, vocab_tile=vocab_tile),
+                     dtype=torch.uint8, device="cuda")
     out = torch.empty(B, dtype=torch.int32, device="cuda")
     for i in range(warmup):
-        fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, out=out, workspace=ws, variant=variant)
+        fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, out=out, workspace=ws, variant=variant,
+                        vocab_tile=vocab_tile)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in ev:  # create the HIP events; the library re-records them around Stage 1
         a.record()
@@ -72,7 +73,7 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto"):
     t0.record()
     for i in range(steps):
         fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, out=out, workspace=ws, variant=variant,
-                        events=ev[i])
+                        vocab_tile=vocab_tile, events=ev[i])
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
@@ -143,8 +144,11 @@ def main():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--sweep", action="store_true", help="also time every B of the workload's sweep")
+    ap.add_argument("--batches", default="", help="comma-separated batch sizes to sweep instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--variant", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--vocab-tile", type=int, default=0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a device copy of this size (counter calibration) and exit")
     args = ap.parse_args()
@@ -175,7 +179,8 @@ def main():
     B = args.batch
     log(f"[bench] generating {wl.name}: D={wl.D} V={wl.V} {wl.dtype}, B={B}")
     t = time.perf_counter()
-    H = inputs.make_hidden(wl, b_max=max(wl.b_max, B))
+    b_need = max([wl.b_max, B] + [int(x) for x in args.batches.split(",") if x])
+    H = inputs.make_hidden(wl, b_max=b_need)
     W = inputs.make_weights(wl)
     log(f"[bench] inputs ready in {time.perf_counter() - t:.1f} s; uploading")
     Hd = upload(H)
@@ -186,8 +191,8 @@ def main():
 
     def run(b):
         Hb = Hd[:b]
-        ms, s1 = time_fused(fs, Hb, Ws, wl, args.steps, args.warmup, b)
-        nt = fs.num_vocab_tiles(b, wl.D, wl.V, Hb.dtype)
+        ms, s1 = time_fused(fs, Hb, Ws, wl, args.steps, args.warmup, b, args.variant, args.vocab_tile)
+        nt = fs.num_vocab_tiles(b, wl.D, wl.V, Hb.dtype, args.variant, args.vocab_tile)
         byts = stage1_bytes(b, wl.D, wl.V, esz, nt)
         rec = {"B": b, "ms_per_step": ms, "samples_per_s": b / (ms * 1e-3), "stage1_ms": s1,
                "stage1_GBps": byts / (s1 * 1e-3) / 1e9, "stage1_bytes": byts, "n_tiles": nt,
@@ -202,7 +207,8 @@ def main():
         return rec
 
     head = run(B)
-    sweep = [run(b) for b in wl.batches if b != B] if args.sweep else []
+    sweep_bs = [int(x) for x in args.batches.split(",") if x] or (list(wl.batches) if args.sweep else [])
+    sweep = [run(b) for b in sweep_bs if b != B]
 
     torch.cuda.synchronize()
     result = {

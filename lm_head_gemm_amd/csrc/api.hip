@@ -16,6 +16,9 @@ constexpr int64_t kMaxV = 0x7FFFFFFF;       // tokens are int32
 constexpr int64_t kMaxD = 1 << 20;
 constexpr int32_t kGemvGranule = 16;        // 4 waves x 4-row groups
 constexpr int32_t kGemvDefaultTile = 64;
+constexpr int32_t kMfmaGranule = 64;
+constexpr int32_t kMfmaDefaultTile = 128;
+constexpr int64_t kGemvMaxB = 4;            // bf16 batches above this use the MFMA kernel
 constexpr int32_t kSamplePart = 2048;       // unfused sampler: vocab entries per workgroup
 constexpr size_t kAlign = 256;
 
@@ -41,26 +44,37 @@ struct Plan {
 };
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
+//   GEMV: fp32 inputs, and bf16 batches up to kGemvMaxB rows;
+//   MFMA: bf16 batches above that (vocab tile 128 rows, or 64 on request).
 bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* o, Plan* p,
                fs_status_t* why) {
   (void)D;
   *why = FS_ERR_INVALID_ARGUMENT;
   int variant = o ? o->variant : FS_VARIANT_AUTO;
   if (variant != FS_VARIANT_AUTO && variant != FS_VARIANT_GEMV && variant != FS_VARIANT_MFMA) return false;
-  if (variant == FS_VARIANT_AUTO) variant = FS_VARIANT_GEMV;
-  (void)B;
+  if (variant == FS_VARIANT_AUTO)
+    variant = (dtype == FS_DTYPE_BF16 && B > kGemvMaxB) ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
+  int32_t tile = o ? o->vocab_tile : 0;
   if (variant == FS_VARIANT_MFMA) {
-    *why = FS_ERR_UNSUPPORTED;
-    return false;
+    if (dtype != FS_DTYPE_BF16) {
+      *why = FS_ERR_UNSUPPORTED;
+      return false;
+    }
+    if (tile == 0) tile = kMfmaDefaultTile;
+    if (tile != mfma_tile_rows(1) && tile != mfma_tile_rows(2)) return false;
+  } else {
+    if (tile == 0) tile = kGemvDefaultTile;
+    if (tile < 0 || tile % kGemvGranule != 0) return false;
   }
-  (void)dtype;
-  int32_t tile = o && o->vocab_tile ? o->vocab_tile : kGemvDefaultTile;
-  if (tile < 0 || tile % kGemvGranule != 0) return false;
   p->variant = (fs_variant_t)variant;
   p->tile = tile;
   p->n_tiles = (V + tile - 1) / tile;
   if (p->n_tiles > 0x7FFFFFFF) return false;
   return true;
+}
+
+hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream) {
+  return p.variant == FS_VARIANT_MFMA ? launch_stage1_mfma(a, stream) : launch_stage1_gemv(a, dtype, stream);
 }
 
 size_t fused_ws_bytes(int64_t B, const Plan& p) {
@@ -140,6 +154,7 @@ int32_t fs_vocab_tile_granule(fs_variant_t variant) {
   switch (variant) {
     case FS_VARIANT_AUTO:
     case FS_VARIANT_GEMV: return kGemvGranule;
+    case FS_VARIANT_MFMA: return kMfmaGranule;
     default: return -1;
   }
 }
@@ -189,7 +204,7 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
   hipError_t e;
   if (opts && opts->stage1_start && (e = hipEventRecord(opts->stage1_start, stream)) != hipSuccess)
     return fail_hip(e);
-  e = launch_stage1_gemv(a, dtype, stream);
+  e = launch_stage1(p, a, dtype, stream);
   if (e != hipSuccess) return fail_hip(e);
   if (opts && opts->stage1_stop && (e = hipEventRecord(opts->stage1_stop, stream)) != hipSuccess)
     return fail_hip(e);
@@ -235,7 +250,7 @@ fs_status_t fs_sample_unfused(const void* H, int64_t ldh, const void* W, int64_t
   a.logits = ws;
   a.ld_logits = ld;
   a.logits_bf16 = logits_dtype == FS_DTYPE_BF16;
-  hipError_t e = launch_stage1_gemv(a, dtype, stream);
+  hipError_t e = launch_stage1(p, a, dtype, stream);
   if (e != hipSuccess) return fail_hip(e);
   // step 2: sampler that reads them back
   e = launch_sample_logits(ws, ld, a.logits_bf16, a.B, a.V, a.inv_t, a.greedy, a.nk, kSamplePart, n_parts,

@@ -145,6 +145,8 @@ struct Stage1Args {
 // Launchers (each returns the hipError_t of its launches).
 hipError_t launch_stage1_gemv(const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream);
 int gemv_batch_tile(int64_t B, int64_t D, fs_dtype_t dtype);
+hipError_t launch_stage1_mfma(const Stage1Args& a, hipStream_t stream);
+int mfma_tile_rows(int blocks_per_wave);
 hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32_t* out,
                          hipStream_t stream);
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,

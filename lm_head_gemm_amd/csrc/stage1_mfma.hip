@@ -1,0 +1,265 @@
+// Stage 1, matrix-core regime: FlashSampling's fused kernel (arXiv
+// 2603.15854, Section 3, "Stage 1 (Fused Kernel)") on CDNA4 bf16 MFMA, for
+// batches large enough that the LM-head product is a real contraction.
+//
+// Tile: one workgroup = BM vocab rows x BN batch rows; 4 waves, each owning
+// 16*MB consecutive vocab rows and all BN batch rows. The product is
+// C[v, b] = sum_d W[v, d] H[b, d] with vocab on the MFMA M axis, so after
+// v_mfma_f32_16x16x32_bf16 a lane holds four consecutive vocab rows of one
+// batch row: exactly the four words of one Philox4x32-10 call.
+//
+// Data flow per K chunk of 256:
+//  * W goes straight from HBM to registers in the MFMA A layout (a lane
+//    reads 16 bytes of its row per K step, four lanes cover 64 contiguous
+//    bytes of a row), one chunk ahead of the math, so each W byte is read
+//    exactly once and never touches LDS;
+//  * the H chunk [BN, 256] is staged by the whole workgroup into LDS (rows
+//    padded by 16 bytes so the B-operand reads are bank-conflict free),
+//    double-buffered, and shared by the four waves.
+// Epilogue in registers: l * (1/T) + Gumbel, packed-key maximum per batch
+// row over the wave's rows, then over the waves through LDS; one candidate
+// per (batch row, vocab tile). Optionally the logits are stored instead of
+// or besides sampling (the unfused baseline's GEMM and the IO-model check).
+//
+// Large batches are split into batch tiles; workgroups that share a vocab
+// tile get consecutive slots on the same XCD so the tile of W is fetched
+// from HBM once and re-read from that XCD's L2.
+#include "fs_common.h"
+
+namespace fs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kKS = 8;               // MFMA K steps (of 32) per K chunk
+constexpr int kBK = 32 * kKS;        // 256
+constexpr int kLdsRow = kBK + 8;     // padded H row in LDS (elements)
+constexpr int kXcds = 8;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Maps the launch index to (vocab tile, batch tile) so that the n_bt batch
+// tiles of one vocab tile run back to back on one XCD (workgroup i goes to
+// XCD i mod 8). Returns false for the padding slots of the grid.
+__device__ __forceinline__ bool tile_of(int L, int n_vt, int n_bt, int* vt, int* bt) {
+  if (n_bt == 1) {
+    *vt = L;
+    *bt = 0;
+    return L < n_vt;
+  }
+  const int G = n_vt * n_bt;
+  const int per = (G + kXcds - 1) / kXcds;
+  const int logical = (L % kXcds) * per + L / kXcds;
+  if (logical >= G) return false;
+  *vt = logical / n_bt;
+  *bt = logical - *vt * n_bt;
+  return true;
+}
+
+template <int NB, int MB, bool SAMPLE, bool STORE>
+__global__ __launch_bounds__(kThreads, 2) void stage1_mfma_kernel(Stage1Args a, int32_t n_bt) {
+  constexpr int BN = 16 * NB;
+  constexpr int BM = kWaves * 16 * MB;
+  constexpr int HPIECES = BN * (kBK / 8) / kThreads;   // 16-byte pieces of H per thread per chunk
+  static_assert(HPIECES >= 1, "batch tile too small");
+
+  __shared__ uint4 lds_h4[2 * BN * kLdsRow / 8];
+  __shared__ uint64_t red[kWaves][BN];
+  uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
+
+  int vt, bt;
+  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int row0 = vt * BM + wave * 16 * MB;   // first vocab row of this wave
+  const int b0 = bt * BN;
+  const int D = a.D;
+  const int nchunk = (D + kBK - 1) / kBK;
+
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  const uint16_t* H = static_cast<const uint16_t*>(a.H);
+  const uint16_t* wrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) wrow[mb] = W + (int64_t)min(row0 + 16 * mb + r, a.V - 1) * a.ldw;
+
+  auto load_w = [&](int c, uint4 (&w)[kKS][MB]) {
+#pragma unroll
+    for (int t = 0; t < kKS; ++t) {
+      const int k = c * kBK + 32 * t + 8 * q;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        w[t][mb] = make_uint4(0u, 0u, 0u, 0u);
+        if (k < D) w[t][mb] = *reinterpret_cast<const uint4*>(wrow[mb] + k);
+      }
+    }
+  };
+  auto load_h = [&](int c, uint4 (&h)[HPIECES]) {
+#pragma unroll
+    for (int i = 0; i < HPIECES; ++i) {
+      const int p = tid + kThreads * i;
+      const int n = p / (kBK / 8);
+      const int k = c * kBK + 8 * (p % (kBK / 8));
+      h[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (b0 + n < a.B && k < D) h[i] = *reinterpret_cast<const uint4*>(H + (int64_t)(b0 + n) * a.ldh + k);
+    }
+  };
+  auto store_h = [&](int buf, const uint4 (&h)[HPIECES]) {
+#pragma unroll
+    for (int i = 0; i < HPIECES; ++i) {
+      const int p = tid + kThreads * i;
+      const int n = p / (kBK / 8);
+      const int kk = 8 * (p % (kBK / 8));
+      *reinterpret_cast<uint4*>(lds_h + buf * BN * kLdsRow + n * kLdsRow + kk) = h[i];
+    }
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wcur[kKS][MB], wnext[kKS][MB];
+  uint4 hreg[HPIECES];
+  load_h(0, hreg);
+  store_h(0, hreg);
+  load_w(0, wcur);
+  __syncthreads();
+
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nchunk;
+    if (more) {
+      load_w(c + 1, wnext);
+      load_h(c + 1, hreg);
+    }
+    const uint16_t* hb = lds_h + buf * BN * kLdsRow;
+#pragma unroll
+    for (int t = 0; t < kKS; ++t) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma16x16x32(wcur[t][mb], bfrag, acc[mb][nb]);
+      }
+    }
+    if (more) store_h(buf ^ 1, hreg);
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < kKS; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) wcur[t][mb] = wnext[t][mb];
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  const int tile_end = min(a.V, vt * BM + BM);
+  if constexpr (STORE) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int b = b0 + nb * 16 + r;
+      if (b >= a.B) continue;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int v0 = row0 + 16 * mb + 4 * q;
+        const f32x4 l = acc[mb][nb];
+        const int64_t off = (int64_t)b * a.ld_logits + v0;
+        if (a.logits_bf16) {
+          uint16_t* p = static_cast<uint16_t*>(a.logits) + off;
+          if (v0 + 3 < tile_end && (off & 3) == 0) {
+            *reinterpret_cast<uint2*>(p) =
+                make_uint2((uint32_t)f32_to_bf16_rne(l[0]) | ((uint32_t)f32_to_bf16_rne(l[1]) << 16),
+                           (uint32_t)f32_to_bf16_rne(l[2]) | ((uint32_t)f32_to_bf16_rne(l[3]) << 16));
+          } else {
+            for (int j = 0; j < 4; ++j)
+              if (v0 + j < tile_end) p[j] = f32_to_bf16_rne(l[j]);
+          }
+        } else {
+          float* p = static_cast<float*>(a.logits) + off;
+          if (v0 + 3 < tile_end && (off & 3) == 0) {
+            *reinterpret_cast<float4*>(p) = make_float4(l[0], l[1], l[2], l[3]);
+          } else {
+            for (int j = 0; j < 4; ++j)
+              if (v0 + j < tile_end) p[j] = l[j];
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (SAMPLE) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int b = b0 + nb * 16 + r;
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int v0 = row0 + 16 * mb + 4 * q;
+        uint4 words = make_uint4(0u, 0u, 0u, 0u);
+        if (!a.greedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float l = acc[mb][nb][j];
+          const float s = a.greedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, j)));
+          const bool valid = v0 + j < tile_end && b < a.B;
+          best = umax64(best, valid ? pack_key(s, (uint32_t)(v0 + j)) : 0ull);
+        }
+      }
+      best = umax64(best, shfl_xor_u64(best, 16));
+      best = umax64(best, shfl_xor_u64(best, 32));
+      if (q == 0) red[wave][nb * 16 + r] = best;
+    }
+    __syncthreads();
+    if (tid < BN && b0 + tid < a.B) {
+      uint64_t k = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) k = umax64(k, red[w][tid]);
+      a.cand[(int64_t)(b0 + tid) * a.n_tiles + vt] = k;
+    }
+  }
+}
+
+template <int NB, int MB>
+hipError_t launch_nb(const Stage1Args& a, hipStream_t stream) {
+  constexpr int BN = 16 * NB;
+  const bool sample = a.cand != nullptr;
+  const bool store = a.logits != nullptr;
+  const int n_bt = (a.B + BN - 1) / BN;
+  const int64_t G = (int64_t)a.n_tiles * n_bt;
+  const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  void (*k)(Stage1Args, int32_t) = nullptr;
+  if (sample && store) k = stage1_mfma_kernel<NB, MB, true, true>;
+  else if (sample) k = stage1_mfma_kernel<NB, MB, true, false>;
+  else k = stage1_mfma_kernel<NB, MB, false, true>;
+  return launch(k, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, (int32_t)n_bt);
+}
+
+template <int MB>
+hipError_t launch_mb(const Stage1Args& a, hipStream_t stream) {
+  if (a.B <= 16) return launch_nb<1, MB>(a, stream);
+  if (a.B <= 32) return launch_nb<2, MB>(a, stream);
+  return launch_nb<4, MB>(a, stream);
+}
+
+}  // namespace
+
+// Vocab rows per MFMA workgroup for a given number of 16-row blocks per wave.
+int mfma_tile_rows(int mb) { return kWaves * 16 * mb; }
+
+hipError_t launch_stage1_mfma(const Stage1Args& a, hipStream_t stream) {
+  if (a.vocab_tile == mfma_tile_rows(1)) return launch_mb<1>(a, stream);
+  return launch_mb<2>(a, stream);
+}
+
+}  // namespace fs

@@ -75,17 +75,44 @@ def test_small_shapes(fs, dtype, B, D, V, T):
         check_parity(H, W, T, seed, step, np.arange(B), tok)
 
 
-@pytest.mark.parametrize("tile", [16, 48, 64, 256, 1008, 4096])
-def test_vocab_tile_invariance(fs, tile):
+@pytest.mark.parametrize("variant,tile", [("gemv", 16), ("gemv", 48), ("gemv", 64), ("gemv", 256),
+                                          ("gemv", 1008), ("gemv", 4096), ("mfma", 64), ("mfma", 128)])
+def test_vocab_tile_invariance(fs, variant, tile):
     B, D, V = 6, 512, 5003
     H, W = _rand_head(7, B, D, V)
     Hd, Wd = to_device(H), to_device(W)
     ref = fs.sample_fused(Hd, Wd, 0.9, 3, 11).cpu().numpy()
-    got = fs.sample_fused(Hd, Wd, 0.9, 3, 11, vocab_tile=tile).cpu().numpy()
+    got = fs.sample_fused(Hd, Wd, 0.9, 3, 11, variant=variant, vocab_tile=tile).cpu().numpy()
     r = oracle.sample(H, W, 0.9, 3, 11)
     firm = r.margin > TOL
     assert np.array_equal(got[firm], ref[firm])
     check_parity(H, W, 0.9, 3, 11, np.arange(B), got)
+
+
+@pytest.mark.parametrize("variant,tile", [("mfma", 64), ("mfma", 128), ("gemv", 64), ("gemv", 1008)])
+@pytest.mark.parametrize("B,D,V", [
+    (1, 64, 5), (5, 520, 2001), (16, 256, 777), (17, 1032, 3000), (64, 4096, 2053),
+    (65, 264, 4099), (130, 512, 1500), (300, 128, 1000),
+])
+def test_forced_variants(fs, variant, tile, B, D, V):
+    """Both Stage-1 kernel families at several tiles, batch tiles, ragged
+    vocab and K tails (D not a multiple of the K chunk)."""
+    H, W = _rand_head(B * 7 + D + V, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    for T, seed, step in ((1.0, 0, 0), (0.6, 77, 2**32 + 1), (0.0, 0, 0)):
+        tok = fs.sample_fused(Hd, Wd, T, seed, step, variant=variant, vocab_tile=tile).cpu().numpy()
+        check_parity(H, W, T, seed, step, np.arange(B), tok)
+
+
+def test_mfma_store_logits_matches_exact(fs):
+    import torch
+    B, D, V = 70, 1032, 1001
+    H, W = _rand_head(5, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    exact = oracle.exact_logits(H, W)
+    l32 = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda")
+    fs.sample_fused(Hd, Wd, 1.0, 0, 0, variant="mfma", logits=l32)
+    assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - exact)) < 1e-4
 
 
 def test_batch_prefix_and_repeat_determinism(fs):
