@@ -72,7 +72,9 @@ typedef struct fs_options {
                               (device [B, V] row-major, stride ld_logits) */
   int64_t ld_logits;
   int32_t logits_dtype;    /* fs_dtype_t of the stored logits */
-  int32_t reserved;
+  int32_t batch_tile;      /* MFMA only: batch rows per workgroup (16, 32 or
+                              64); 0 = chosen from B. Larger batches are split
+                              into tiles that re-read W from L2. */
   hipEvent_t stage1_start; /* non-null: recorded on `stream` right before and */
   hipEvent_t stage1_stop;  /* right after the Stage-1 launch (for timing) */
 } fs_options_t;
@@ -104,7 +106,7 @@ size_t fs_workspace_bytes_ex(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
  *   H, ldh, W, ldw, dtype, B, D, V: as in the conventions above.
  *   temperature: T >= 0 and finite (T == 0: greedy).
  *   seed, step: noise key and decode step (see the noise paragraph above).
- *   workspace: device, >= fs_workspace_bytes(...) bytes, 256-byte aligned.
+ *   workspace: device, >= fs_workspace_bytes(...) bytes, 16-byte aligned.
  *   out_tokens: device int32 [B].
  * Errors: FS_ERR_INVALID_ARGUMENT, FS_ERR_UNSUPPORTED,
  *         FS_ERR_WORKSPACE_TOO_SMALL, FS_ERR_HIP. */
@@ -147,6 +149,16 @@ fs_status_t fs_sample_unfused(const void* H, int64_t ldh, const void* W, int64_t
 fs_status_t fs_test_philox(uint64_t seed, uint64_t step, int64_t b, int64_t v0, int64_t n,
                            uint32_t* words_out, hipStream_t stream);
 fs_status_t fs_test_gumbel(const uint32_t* words, int64_t n, float* g_out, hipStream_t stream);
+
+/* Measurement hook: reads `bytes` (multiple of 16) from the device buffer
+ * src with 16-byte loads, workgroup g covering [g*chunk_bytes,
+ * (g+1)*chunk_bytes), and writes one folded word per workgroup to sink
+ * (device, fs_probe_read_blocks(bytes, chunk_bytes) words). It moves exactly
+ * the bytes of a W-sized read and nothing else, which gives the attainable
+ * streaming bandwidth and a reference for hardware traffic counters. */
+int64_t fs_probe_read_blocks(int64_t bytes, int64_t chunk_bytes);
+fs_status_t fs_probe_read(const void* src, int64_t bytes, int64_t chunk_bytes, uint32_t* sink,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

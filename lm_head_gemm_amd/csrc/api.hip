@@ -15,10 +15,11 @@ constexpr int64_t kMaxB = 65536;
 constexpr int64_t kMaxV = 0x7FFFFFFF;       // tokens are int32
 constexpr int64_t kMaxD = 1 << 20;
 constexpr int32_t kGemvGranule = 16;        // 4 waves x 4-row groups
-constexpr int32_t kGemvDefaultTile = 64;
+constexpr int32_t kGemvDefaultTile = 16;
 constexpr int32_t kMfmaGranule = 64;
-constexpr int32_t kMfmaDefaultTile = 128;
-constexpr int64_t kGemvMaxB = 4;            // bf16 batches above this use the MFMA kernel
+constexpr int32_t kMfmaSmallBTile = 64;    // one 16-row block per wave
+constexpr int32_t kMfmaLargeBTile = 128;    // two blocks per wave above 32 rows
+constexpr int64_t kGemvMaxB = 2;            // bf16 batches above this use the MFMA kernel
 constexpr int32_t kSamplePart = 2048;       // unfused sampler: vocab entries per workgroup
 constexpr size_t kAlign = 256;
 
@@ -41,6 +42,7 @@ struct Plan {
   fs_variant_t variant;
   int32_t tile;
   int64_t n_tiles;
+  int32_t batch_tile = 0;
 };
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
@@ -60,8 +62,11 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
       *why = FS_ERR_UNSUPPORTED;
       return false;
     }
-    if (tile == 0) tile = kMfmaDefaultTile;
+    if (tile == 0) tile = B > 32 ? kMfmaLargeBTile : kMfmaSmallBTile;
     if (tile != mfma_tile_rows(1) && tile != mfma_tile_rows(2)) return false;
+    const int32_t bt = o ? o->batch_tile : 0;
+    if (bt != 0 && bt != 16 && bt != 32 && bt != 64) return false;
+    p->batch_tile = bt;
   } else {
     if (tile == 0) tile = kGemvDefaultTile;
     if (tile < 0 || tile % kGemvGranule != 0) return false;
@@ -127,6 +132,7 @@ Stage1Args stage1_args(const void* H, int64_t ldh, const void* W, int64_t ldw, i
   a.nk = noise_key(seed, step);
   a.vocab_tile = p.tile;
   a.n_tiles = (int32_t)p.n_tiles;
+  a.batch_tile = p.batch_tile;
   return a;
 }
 
@@ -272,6 +278,20 @@ fs_status_t fs_test_philox(uint64_t seed, uint64_t step, int64_t b, int64_t v0, 
 fs_status_t fs_test_gumbel(const uint32_t* words, int64_t n, float* g_out, hipStream_t stream) {
   if (!words || !g_out || n <= 0 || n > ((int64_t)1 << 32)) return FS_ERR_INVALID_ARGUMENT;
   hipError_t e = launch_test_gumbel(words, n, g_out, stream);
+  return e == hipSuccess ? FS_OK : fail_hip(e);
+}
+
+int64_t fs_probe_read_blocks(int64_t bytes, int64_t chunk_bytes) {
+  if (bytes <= 0 || chunk_bytes <= 0 || bytes % 16 || chunk_bytes % 16) return -1;
+  const int64_t n = (bytes + chunk_bytes - 1) / chunk_bytes;
+  return n > 0x7FFFFFFF ? -1 : n;
+}
+
+fs_status_t fs_probe_read(const void* src, int64_t bytes, int64_t chunk_bytes, uint32_t* sink,
+                          hipStream_t stream) {
+  if (!src || !sink || fs_probe_read_blocks(bytes, chunk_bytes) < 0) return FS_ERR_INVALID_ARGUMENT;
+  if (!aligned16(src)) return FS_ERR_UNSUPPORTED;
+  hipError_t e = launch_probe_read(src, bytes, chunk_bytes, sink, stream);
   return e == hipSuccess ? FS_OK : fail_hip(e);
 }
 

@@ -99,6 +99,16 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// ------------------------------------------------------------------ streaming loads
+// W is read exactly once per call: non-temporal 16-byte loads keep it from
+// displacing reusable lines in L2 and stream measurably faster from HBM.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
@@ -136,6 +146,7 @@ struct Stage1Args {
   NoiseKey nk;
   int32_t vocab_tile;   // rows per tile
   int32_t n_tiles;
+  int32_t batch_tile;   // MFMA: batch rows per workgroup (0: from B)
   uint64_t* cand;       // [B, n_tiles] keys, or null (store-only)
   void* logits;         // [B, V] logits, or null
   int64_t ld_logits;
@@ -156,5 +167,7 @@ hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_b
 hipError_t launch_test_philox(NoiseKey nk, uint32_t b, int64_t v0, int64_t n, uint32_t* out,
                               hipStream_t stream);
 hipError_t launch_test_gumbel(const uint32_t* words, int64_t n, float* out, hipStream_t stream);
+hipError_t launch_probe_read(const void* src, int64_t bytes, int64_t chunk_bytes, uint32_t* sink,
+                             hipStream_t stream);
 
 }  // namespace fs

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
           w[jj][r] = make_uint4(0u, 0u, 0u, 0u);
-          if (c < nch) w[jj][r] = *reinterpret_cast<const uint4*>(wp[r] + (int64_t)c * 16);
+          if (c < nch) w[jj][r] = load_stream16(wp[r] + (int64_t)c * 16);
         }
       }
 #pragma unroll

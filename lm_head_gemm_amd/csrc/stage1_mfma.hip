@@ -9,10 +9,13 @@
 // batch row: exactly the four words of one Philox4x32-10 call.
 //
 // Data flow per K chunk of 256:
-//  * W goes straight from HBM to registers in the MFMA A layout (a lane
-//    reads 16 bytes of its row per K step, four lanes cover 64 contiguous
-//    bytes of a row), one chunk ahead of the math, so each W byte is read
-//    exactly once and never touches LDS;
+//  * W is read from HBM with coalesced non-temporal loads (one wave load =
+//    512 contiguous bytes of each of two rows), one chunk ahead of the math,
+//    so each W byte is read exactly once; the wave then transposes its own
+//    rows through a private LDS region (16-byte pieces XOR-swizzled by row,
+//    conflict-free on both sides) into the MFMA A layout. Reading W directly
+//    in the A layout (64 bytes of 16 rows per load) streams measurably
+//    slower from HBM than whole 512-byte row pieces;
 //  * the H chunk [BN, 256] is staged by the whole workgroup into LDS (rows
 //    padded by 16 bytes so the B-operand reads are bank-conflict free),
 //    double-buffered, and shared by the four waves.
@@ -66,10 +69,13 @@ template <int NB, int MB, bool SAMPLE, bool STORE>
 __global__ __launch_bounds__(kThreads, 2) void stage1_mfma_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int BN = 16 * NB;
   constexpr int BM = kWaves * 16 * MB;
+  constexpr int WROWS = 16 * MB;                        // vocab rows per wave
+  constexpr int WLOADS = WROWS / 2;                     // W loads per lane per chunk
   constexpr int HPIECES = BN * (kBK / 8) / kThreads;   // 16-byte pieces of H per thread per chunk
   static_assert(HPIECES >= 1, "batch tile too small");
 
   __shared__ uint4 lds_h4[2 * BN * kLdsRow / 8];
+  __shared__ uint4 lds_w4[kWaves * WROWS * (kBK / 8)];  // per-wave transpose regions
   __shared__ uint64_t red[kWaves][BN];
   uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
 
@@ -81,26 +87,37 @@ __global__ __launch_bounds__(kThreads, 2) void stage1_mfma_kernel(Stage1Args a, 
   const int wave = tid >> 6;
   const int r = lane & 15;
   const int q = lane >> 4;
-  const int row0 = vt * BM + wave * 16 * MB;   // first vocab row of this wave
+  const int row0 = vt * BM + wave * WROWS;   // first vocab row of this wave
   const int b0 = bt * BN;
   const int D = a.D;
   const int nchunk = (D + kBK - 1) / kBK;
 
   const uint16_t* W = static_cast<const uint16_t*>(a.W);
   const uint16_t* H = static_cast<const uint16_t*>(a.H);
-  const uint16_t* wrow[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) wrow[mb] = W + (int64_t)min(row0 + 16 * mb + r, a.V - 1) * a.ldw;
+  uint4* wl = lds_w4 + wave * WROWS * (kBK / 8);
 
-  auto load_w = [&](int c, uint4 (&w)[kKS][MB]) {
+  // load i of a chunk covers rows 2i (lanes 0..31) and 2i+1 (lanes 32..63)
+  const int lrow = lane >> 5;
+  const int piece = lane & 31;
+  const uint16_t* wsrc[WLOADS];
 #pragma unroll
-    for (int t = 0; t < kKS; ++t) {
-      const int k = c * kBK + 32 * t + 8 * q;
+  for (int i = 0; i < WLOADS; ++i)
+    wsrc[i] = W + (int64_t)min(row0 + 2 * i + lrow, a.V - 1) * a.ldw + 8 * piece;
+
+  auto load_w = [&](int c, uint4 (&w)[WLOADS]) {
+    const int k = c * kBK + 8 * piece;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        w[t][mb] = make_uint4(0u, 0u, 0u, 0u);
-        if (k < D) w[t][mb] = *reinterpret_cast<const uint4*>(wrow[mb] + k);
-      }
+    for (int i = 0; i < WLOADS; ++i) {
+      w[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (k < D) w[i] = load_stream16(wsrc[i] + c * kBK);
+    }
+  };
+  // slot of 16-byte piece p of wave-local row rho: p ^ (rho & 15)
+  auto store_w = [&](const uint4 (&w)[WLOADS]) {
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i) {
+      const int rho = 2 * i + lrow;
+      wl[rho * (kBK / 8) + (piece ^ (rho & 15))] = w[i];
     }
   };
   auto load_h = [&](int c, uint4 (&h)[HPIECES]) {
@@ -129,38 +146,49 @@ __global__ __launch_bounds__(kThreads, 2) void stage1_mfma_kernel(Stage1Args a, 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wcur[kKS][MB], wnext[kKS][MB];
+  // Two register sets for W alternate between "in flight" and "being
+  // transposed", so the loads of chunk c+1 stay outstanding during chunk c.
+  uint4 wa[WLOADS], wb[WLOADS];
   uint4 hreg[HPIECES];
   load_h(0, hreg);
   store_h(0, hreg);
-  load_w(0, wcur);
+  load_w(0, wa);
   __syncthreads();
 
-  for (int c = 0; c < nchunk; ++c) {
+  auto step = [&](int c, uint4 (&wcur)[WLOADS], uint4 (&wnext)[WLOADS]) {
     const int buf = c & 1;
     const bool more = c + 1 < nchunk;
     if (more) {
-      load_w(c + 1, wnext);
+      // H first: its registers are needed (for the LDS store) before the
+      // next chunk of W, and loads complete in issue order
       load_h(c + 1, hreg);
+      load_w(c + 1, wnext);
     }
+    // the wave's own region: its previous reads were issued before these
+    // writes and LDS operations of one wave execute in order
+    store_w(wcur);
     const uint16_t* hb = lds_h + buf * BN * kLdsRow;
 #pragma unroll
     for (int t = 0; t < kKS; ++t) {
+      uint4 afrag[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int rho = 16 * mb + r;
+        afrag[mb] = wl[rho * (kBK / 8) + ((4 * t + q) ^ (rho & 15))];
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma16x16x32(wcur[t][mb], bfrag, acc[mb][nb]);
+        for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma16x16x32(afrag[mb], bfrag, acc[mb][nb]);
       }
     }
     if (more) store_h(buf ^ 1, hreg);
     __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int t = 0; t < kKS; ++t)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) wcur[t][mb] = wnext[t][mb];
-    }
+  };
+  for (int c = 0; c < nchunk; c += 2) {
+    step(c, wa, wb);
+    if (c + 1 < nchunk) step(c + 1, wb, wa);
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -247,8 +275,9 @@ hipError_t launch_nb(const Stage1Args& a, hipStream_t stream) {
 
 template <int MB>
 hipError_t launch_mb(const Stage1Args& a, hipStream_t stream) {
-  if (a.B <= 16) return launch_nb<1, MB>(a, stream);
-  if (a.B <= 32) return launch_nb<2, MB>(a, stream);
+  const int bn = a.batch_tile ? a.batch_tile : (a.B <= 16 ? 16 : a.B <= 32 ? 32 : 64);
+  if (bn == 16) return launch_nb<1, MB>(a, stream);
+  if (bn == 32) return launch_nb<2, MB>(a, stream);
   return launch_nb<4, MB>(a, stream);
 }
 

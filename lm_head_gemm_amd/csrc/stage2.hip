@@ -10,24 +10,37 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One workgroup per batch row; keys are read with 256 lanes in parallel.
-__global__ __launch_bounds__(kThreads) void stage2_kernel(const uint64_t* __restrict__ cand,
-                                                          int32_t n_tiles,
-                                                          int32_t* __restrict__ out) {
-  __shared__ uint64_t red[kThreads / 64];
+// One workgroup of 1024 lanes per batch row; each lane folds its keys with
+// four independent loads in flight, so a row of several thousand tile
+// candidates costs about one memory round trip.
+constexpr int kS2Threads = 1024;
+
+__global__ __launch_bounds__(kS2Threads) void stage2_kernel(const uint64_t* __restrict__ cand,
+                                                            int32_t n_tiles,
+                                                            int32_t* __restrict__ out) {
+  __shared__ uint64_t red[kS2Threads / 64];
   const int row = blockIdx.x;
   const uint64_t* c = cand + (int64_t)row * n_tiles;
   uint64_t best = 0ull;
-  for (int t = threadIdx.x; t < n_tiles; t += kThreads) best = umax64(best, c[t]);
+  for (int t0 = threadIdx.x; t0 < n_tiles; t0 += 4 * kS2Threads) {
+    uint64_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * kS2Threads;
+      k[u] = t < n_tiles ? c[t] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) best = umax64(best, k[u]);
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t k = red[0];
+  if (threadIdx.x < 64) {
+    uint64_t k = threadIdx.x < kS2Threads / 64 ? red[threadIdx.x] : 0ull;
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) k = umax64(k, red[w]);
-    out[row] = key_to_token(k);
+    for (int m = 8; m >= 1; m >>= 1) k = umax64(k, shfl_xor_u64(k, m));
+    if (threadIdx.x == 0) out[row] = key_to_token(k);
   }
 }
 
@@ -98,11 +111,48 @@ __global__ __launch_bounds__(kThreads) void test_gumbel_kernel(const uint32_t* w
   out[i] = gumbel_from_word(words[i]);
 }
 
+// Streams `bytes` from src with 16-byte loads and folds them into one word per
+// workgroup: the attainable read bandwidth for a W-sized buffer, and a kernel
+// of exactly known HBM read traffic for counter calibration. Workgroup g reads
+// the contiguous range [g * chunk, (g + 1) * chunk).
+template <int U>
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                              int64_t chunk16, uint32_t* __restrict__ sink) {
+  const int64_t begin = (int64_t)blockIdx.x * chunk16;
+  const int64_t end = min(n16, begin + chunk16);
+  uint32_t x = 0;
+  for (int64_t i = begin + threadIdx.x; i < end; i += (int64_t)kThreads * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = i + (int64_t)u * kThreads;
+      v[u] = j < end ? load_stream16(src + j) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x ^= __shfl_xor(x, m);
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
 }  // namespace
+
+hipError_t launch_probe_read(const void* src, int64_t bytes, int64_t chunk_bytes, uint32_t* sink,
+                             hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  const int64_t chunk16 = chunk_bytes / 16;
+  const dim3 grid((unsigned)((n16 + chunk16 - 1) / chunk16));
+  return launch(probe_read_kernel<8>, grid, dim3(kThreads), 0, stream, static_cast<const uint4*>(src), n16,
+                chunk16, sink);
+}
 
 hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32_t* out,
                          hipStream_t stream) {
-  return launch(stage2_kernel, dim3(B), dim3(kThreads), 0, stream, cand, n_tiles, out);
+  return launch(stage2_kernel, dim3(B), dim3(kS2Threads), 0, stream, cand, n_tiles, out);
 }
 
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,

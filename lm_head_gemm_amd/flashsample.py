@@ -38,7 +38,7 @@ class FsOptions(ctypes.Structure):
         ("logits", ctypes.c_void_p),
         ("ld_logits", ctypes.c_int64),
         ("logits_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("batch_tile", ctypes.c_int32),
         ("stage1_start", ctypes.c_void_p),
         ("stage1_stop", ctypes.c_void_p),
     ]
@@ -84,6 +84,10 @@ def _load():
     lib.fs_test_philox.argtypes = [c_u64, c_u64, c_i64, c_i64, c_i64, vp, vp]
     lib.fs_test_gumbel.restype = ctypes.c_int
     lib.fs_test_gumbel.argtypes = [vp, c_i64, vp, vp]
+    lib.fs_probe_read_blocks.restype = c_i64
+    lib.fs_probe_read_blocks.argtypes = [c_i64, c_i64]
+    lib.fs_probe_read.restype = ctypes.c_int
+    lib.fs_probe_read.argtypes = [vp, c_i64, c_i64, vp, vp]
     return lib
 
 
@@ -119,10 +123,11 @@ def _check_inputs(H: torch.Tensor, W: torch.Tensor):
         raise ValueError("H and W rows must be contiguous")
 
 
-def make_options(variant="auto", vocab_tile=0, logits=None, events=None) -> FsOptions:
+def make_options(variant="auto", vocab_tile=0, logits=None, events=None, batch_tile=0) -> FsOptions:
     o = FsOptions()
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     o.vocab_tile = int(vocab_tile)
+    o.batch_tile = int(batch_tile)
     if logits is not None:
         o.logits = logits.data_ptr()
         o.ld_logits = logits.stride(0)
@@ -150,12 +155,12 @@ def unfused_workspace_bytes(B, D, V, dtype=torch.bfloat16, logits_dtype=torch.bf
 def sample_fused(H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                  variant="auto", vocab_tile: int = 0, logits: torch.Tensor | None = None,
-                 events=None, stream=None) -> torch.Tensor:
+                 events=None, stream=None, batch_tile: int = 0) -> torch.Tensor:
     """One token per row of H from softmax(H W^T / T) (Gumbel-max, fused)."""
     _check_inputs(H, W)
     B, D = H.shape
     V = W.shape[0]
-    o = make_options(variant, vocab_tile, logits, events)
+    o = make_options(variant, vocab_tile, logits, events, batch_tile)
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=H.device)
     if workspace is None:
@@ -201,3 +206,18 @@ def test_gumbel(words: torch.Tensor) -> torch.Tensor:
     _check(_lib.fs_test_gumbel(words.data_ptr(), words.numel(), out.data_ptr(), _stream(None)),
            "fs_test_gumbel")
     return out
+
+
+def probe_read(src: torch.Tensor, chunk_bytes: int = 1 << 19, sink: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """Streams all bytes of a contiguous device tensor (see fs_probe_read)."""
+    assert src.is_cuda and src.is_contiguous()
+    nbytes = src.numel() * src.element_size()
+    nblk = int(_lib.fs_probe_read_blocks(nbytes, chunk_bytes))
+    if nblk < 0:
+        raise ValueError("probe_read: bytes and chunk must be positive multiples of 16")
+    if sink is None:
+        sink = torch.empty(nblk, dtype=torch.int32, device=src.device)
+    _check(_lib.fs_probe_read(src.data_ptr(), nbytes, chunk_bytes, sink.data_ptr(), _stream(stream)),
+           "fs_probe_read")
+    return sink
