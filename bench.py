@@ -2,11 +2,14 @@
 
 A step is one fused sampling call (Stage 1 + Stage 2) over one batch of
 synthetic hidden states against a resident LM head. Default workload: the
-Llama-3-8B-shaped head (D=4096, V=128256, bf16) at B=64. Prints ONE JSON
-line with samples/s, the Stage-1 kernel's achieved HBM bandwidth against
-MI355X's 8 TB/s, the unfused baseline beside it and the CPU oracle's rate.
+Llama-3-8B-shaped head (D=4096, V=128256, bf16) at B=64, with W held in the
+tiled matrix-core layout (repacked once, before timing; --layout rows times
+the row-major path). Prints ONE JSON line with samples/s, the Stage-1
+kernel's achieved HBM bandwidth against MI355X's 8 TB/s, the unfused
+baseline and the row-major layout beside it, and the CPU oracle's rate.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--batch B] [--sweep]
+                  [--layout tiled|rows] [--probe]
 """
 from __future__ import annotations
 
@@ -62,8 +65,9 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
     stream (those extra records are kept out of the step time)."""
     import torch
     T, seed = wl.temperature, wl.seed
-    ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, variant=variant, vocab_tile=vocab_tile),
-                     dtype=torch.uint8, device="cuda")
+    tiled = isinstance(Ws[0], fs.TiledWeights)
+    ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, variant=variant, vocab_tile=vocab_tile,
+                                        tiled=tiled), dtype=torch.uint8, device="cuda")
     out = torch.empty(B, dtype=torch.int32, device="cuda")
     kw = dict(out=out, workspace=ws, variant=variant, vocab_tile=vocab_tile, batch_tile=batch_tile)
     for i in range(warmup):
@@ -159,8 +163,13 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "gemv", "mfma"])
     ap.add_argument("--vocab-tile", type=int, default=0)
     ap.add_argument("--batch-tile", type=int, default=0)
+    ap.add_argument("--layout", default="tiled", choices=["rows", "tiled"],
+                    help="W row-major, or repacked once into the tiled matrix-core layout")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a device copy of this size (counter calibration) and exit")
+    ap.add_argument("--probe", action="store_true",
+                    help="also stream W once per step with the read probe (attainable bandwidth)")
+    ap.add_argument("--no-rows", action="store_true", help="skip timing the row-major layout beside")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -199,23 +208,34 @@ def main():
     Ws = [upload(W), upload(W)]
     esz = 2 if wl.dtype == "bf16" else 4
 
-    def run(b):
+    def run(b, weights=None):
+        weights = Ws if weights is None else weights
         Hb = Hd[:b]
-        ms, s1 = time_fused(fs, Hb, Ws, wl, args.steps, args.warmup, b, args.variant, args.vocab_tile,
+        ms, s1 = time_fused(fs, Hb, weights, wl, args.steps, args.warmup, b, args.variant, args.vocab_tile,
                             args.batch_tile)
-        nt = fs.num_vocab_tiles(b, wl.D, wl.V, Hb.dtype, args.variant, args.vocab_tile)
+        tiled = isinstance(weights[0], fs.TiledWeights)
+        nt = fs.num_vocab_tiles(b, wl.D, wl.V, Hb.dtype, args.variant, args.vocab_tile, tiled=tiled)
         byts = stage1_bytes(b, wl.D, wl.V, esz, nt)
         rec = {"B": b, "ms_per_step": ms, "samples_per_s": b / (ms * 1e-3), "stage1_ms": s1,
                "stage1_GBps": byts / (s1 * 1e-3) / 1e9, "stage1_bytes": byts, "n_tiles": nt,
                "flops": 2 * b * wl.V * wl.D}
         if not args.no_unfused:
-            u16 = time_unfused(fs, Hb, Ws, wl, args.steps, args.warmup, b, torch.bfloat16)
+            u16 = time_unfused(fs, Hb, weights, wl, args.steps, args.warmup, b, torch.bfloat16)
             rec["unfused_bf16_ms_per_step"] = u16
             rec["fused_speedup_vs_unfused_bf16"] = u16 / ms
         log(f"[bench] B={b}: {ms * 1e3:.1f} us/step, stage1 {s1 * 1e3:.1f} us "
             f"({rec['stage1_GBps']:.0f} GB/s)" +
             (f", unfused {rec['unfused_bf16_ms_per_step'] * 1e3:.1f} us" if not args.no_unfused else ""))
         return rec
+
+    Ws_rows = Ws
+    if args.layout == "tiled":
+        Ws = [fs.TiledWeights(w) for w in Ws_rows]
+        torch.cuda.synchronize()
+        if args.no_rows:
+            del Ws_rows
+            Ws_rows = None
+            torch.cuda.empty_cache()
 
     head = run(B)
     sweep_bs = [int(x) for x in args.batches.split(",") if x] or (list(wl.batches) if args.sweep else [])
@@ -236,13 +256,37 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded Gaussian head, FS-DATA-1)",
         "config": {"workload": wl.name, "B": B, "D": wl.D, "V": wl.V, "temperature": wl.temperature,
-                   "vocab_tiles": head["n_tiles"], "W_copies_alternated": 2},
+                   "weights_layout": args.layout, "vocab_tiles": head["n_tiles"], "W_copies_alternated": 2},
         "roofline": {"bound": "hbm", "achieved": head["stage1_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["stage1_GBps"] / HBM_PEAK_GBS,
                      "traffic": traffic_record("stage1", wl.name, B),
                      "kernel": "stage1 (fused GEMM + Gumbel-max epilogue)",
                      "stage1_us": head["stage1_ms"] * 1e3},
     }
+    if args.layout == "tiled" and Ws_rows is not None:
+        rows = run(B, Ws_rows)
+        result["rows_layout"] = {"ms_per_step": rows["ms_per_step"], "samples_per_s": rows["samples_per_s"],
+                                 "stage1_us": rows["stage1_ms"] * 1e3, "stage1_GBps": rows["stage1_GBps"]}
+    if args.probe:
+        if Ws_rows is not None:
+            src = Ws_rows[0]
+        else:
+            src = Ws[0].data if isinstance(Ws[0], fs.TiledWeights) else Ws[0]
+        flat = src.reshape(-1)
+        sink = fs.probe_read(flat)
+        for _ in range(5):
+            fs.probe_read(flat, sink=sink)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            fs.probe_read(flat, sink=sink)
+        t1.record()
+        torch.cuda.synchronize()
+        pms = t0.elapsed_time(t1) / args.steps
+        nbytes = flat.numel() * flat.element_size()
+        result["read_probe"] = {"bytes": nbytes, "us": pms * 1e3, "GBps": nbytes / (pms * 1e-3) / 1e9}
     if "unfused_bf16_ms_per_step" in head:
         result["unfused_bf16"] = {"ms_per_step": head["unfused_bf16_ms_per_step"],
                                   "samples_per_s": B / (head["unfused_bf16_ms_per_step"] * 1e-3),

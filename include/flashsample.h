@@ -60,6 +60,14 @@ typedef enum fs_dtype { FS_DTYPE_BF16 = 0, FS_DTYPE_F32 = 1 } fs_dtype_t;
 /* Stage-1 kernel family. AUTO picks by dtype and batch size. */
 typedef enum fs_variant { FS_VARIANT_AUTO = 0, FS_VARIANT_GEMV = 1, FS_VARIANT_MFMA = 2 } fs_variant_t;
 
+/* Layout of the W argument.
+ *  ROWS:  row-major [V, D] with row stride ldw (the default).
+ *  TILED: the one-time repacked copy made by fs_pack_weights_tiled (bf16
+ *         only): blocks of 16 vocab rows x 256 columns, each 8 KiB
+ *         contiguous in matrix-core operand order; block (m, c) at index
+ *         ((m / 8) * ceil(D / 256) + c) * 8 + m % 8; ldw is ignored. */
+typedef enum fs_layout { FS_LAYOUT_ROWS = 0, FS_LAYOUT_TILED = 1 } fs_layout_t;
+
 /* Options for the _ex entry points; a zero-initialised struct means defaults.
  * Results never depend on variant or vocab_tile (the argmax decomposes over
  * any vocab partition), only speed does. */
@@ -77,6 +85,8 @@ typedef struct fs_options {
                               into tiles that re-read W from L2. */
   hipEvent_t stage1_start; /* non-null: recorded on `stream` right before and */
   hipEvent_t stage1_stop;  /* right after the Stage-1 launch (for timing) */
+  int32_t weights_layout;  /* fs_layout_t of W */
+  int32_t reserved;        /* must be 0 */
 } fs_options_t;
 
 /* Human-readable name of a status code (static storage). */
@@ -87,8 +97,9 @@ const char* fs_status_string(fs_status_t status);
 int fs_last_hip_error(void);
 
 /* Number of Stage-1 vocab tiles the fused call uses for these sizes (the
- * candidate buffer is [B, n_tiles] 64-bit keys at the start of the
- * workspace). Returns -1 for invalid sizes or options. */
+ * candidate buffer is [n_tiles, B] 64-bit keys at the start of the
+ * workspace, tile-major so each Stage-1 workgroup writes one contiguous
+ * run). Returns -1 for invalid sizes or options. */
 int64_t fs_num_vocab_tiles(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
                            const fs_options_t* opts);
 
@@ -125,6 +136,20 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
                                int32_t* out_tokens, hipStream_t stream,
                                const fs_options_t* opts);
 
+/* Bytes of the tiled copy of a [V, D] bf16 LM head (V rounded up to a
+ * group of 8 blocks of 16 rows, D to 256 columns, zero padded). 0 for
+ * invalid sizes or fp32. */
+size_t fs_tiled_weights_bytes(int64_t V, int64_t D, fs_dtype_t dtype);
+
+/* Repacks a row-major bf16 W [V, D] (stride ldw) into the tiled layout
+ * (device buffer `tiled` of at least fs_tiled_weights_bytes bytes, 16-byte
+ * aligned). Weights are static, so this runs once when the head is loaded;
+ * the sampling entry points then take the tiled copy with
+ * weights_layout = FS_LAYOUT_TILED and read it with one contiguous 1 KiB
+ * load per wave per matrix-core step. Errors as fs_sample_fused. */
+fs_status_t fs_pack_weights_tiled(const void* W, int64_t ldw, int64_t V, int64_t D, fs_dtype_t dtype,
+                                  void* tiled, size_t tiled_bytes, hipStream_t stream);
+
 /* Workspace of the unfused baseline: the [B, V] logits in logits_dtype plus
  * the sampler's partial candidates. 0 on invalid sizes. */
 size_t fs_unfused_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
@@ -142,6 +167,16 @@ fs_status_t fs_sample_unfused(const void* H, int64_t ldh, const void* W, int64_t
                               fs_dtype_t logits_dtype,
                               void* workspace, size_t workspace_bytes,
                               int32_t* out_tokens, hipStream_t stream);
+
+/* Same, with options (weights_layout, forced variant and tiles; the logits
+ * and event fields are ignored). */
+fs_status_t fs_sample_unfused_ex(const void* H, int64_t ldh, const void* W, int64_t ldw,
+                                 fs_dtype_t dtype, int64_t B, int64_t D, int64_t V,
+                                 float temperature, uint64_t seed, uint64_t step,
+                                 fs_dtype_t logits_dtype,
+                                 void* workspace, size_t workspace_bytes,
+                                 int32_t* out_tokens, hipStream_t stream,
+                                 const fs_options_t* opts);
 
 /* Test hooks (device buffers): the Philox words the kernels use for
  * vocab indices v0 .. v0+n-1 of row b, and the fp32 Gumbel map the kernels

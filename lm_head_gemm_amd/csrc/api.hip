@@ -17,6 +17,8 @@ constexpr int64_t kMaxD = 1 << 20;
 constexpr int32_t kGemvGranule = 16;        // 4 waves x 4-row groups
 constexpr int32_t kGemvDefaultTile = 16;
 constexpr int32_t kMfmaGranule = 64;
+constexpr int32_t kTiledGemvTile = 128;    // tiled layout: 8 waves x 16 rows
+constexpr int32_t kTiledMfmaTile = 128;     // tiled layout: 8 waves x 16 rows
 constexpr int32_t kMfmaSmallBTile = 64;    // one 16-row block per wave
 constexpr int32_t kMfmaLargeBTile = 128;    // two blocks per wave above 32 rows
 constexpr int64_t kGemvMaxB = 2;            // bf16 batches above this use the MFMA kernel
@@ -43,30 +45,42 @@ struct Plan {
   int32_t tile;
   int64_t n_tiles;
   int32_t batch_tile = 0;
+  bool tiled = false;     // W in the tiled layout
 };
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
-//   GEMV: fp32 inputs, and bf16 batches up to kGemvMaxB rows;
-//   MFMA: bf16 batches above that (vocab tile 128 rows, or 64 on request).
+//   Row-major W: GEMV for fp32 inputs and bf16 batches up to kGemvMaxB rows
+//     (vocab tile: multiple of 16 rows), MFMA above (64 or 128 rows).
+//   Tiled W (bf16): the same split; vocab tile 64 or 128 rows (4 or 8 waves
+//     of one 16-row block each).
 bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* o, Plan* p,
                fs_status_t* why) {
   (void)D;
   *why = FS_ERR_INVALID_ARGUMENT;
+  const int layout = o ? o->weights_layout : FS_LAYOUT_ROWS;
+  if (layout != FS_LAYOUT_ROWS && layout != FS_LAYOUT_TILED) return false;
+  if (o && o->reserved != 0) return false;
   int variant = o ? o->variant : FS_VARIANT_AUTO;
   if (variant != FS_VARIANT_AUTO && variant != FS_VARIANT_GEMV && variant != FS_VARIANT_MFMA) return false;
   if (variant == FS_VARIANT_AUTO)
     variant = (dtype == FS_DTYPE_BF16 && B > kGemvMaxB) ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
   int32_t tile = o ? o->vocab_tile : 0;
-  if (variant == FS_VARIANT_MFMA) {
+  const int32_t bt = o ? o->batch_tile : 0;
+  if (bt != 0 && bt != 16 && bt != 32 && bt != 64) return false;
+  if (layout == FS_LAYOUT_TILED) {
+    if (dtype != FS_DTYPE_BF16) {
+      *why = FS_ERR_UNSUPPORTED;
+      return false;
+    }
+    if (tile == 0) tile = variant == FS_VARIANT_MFMA ? kTiledMfmaTile : kTiledGemvTile;
+    if (tile != 64 && tile != 128) return false;
+  } else if (variant == FS_VARIANT_MFMA) {
     if (dtype != FS_DTYPE_BF16) {
       *why = FS_ERR_UNSUPPORTED;
       return false;
     }
     if (tile == 0) tile = B > 32 ? kMfmaLargeBTile : kMfmaSmallBTile;
     if (tile != mfma_tile_rows(1) && tile != mfma_tile_rows(2)) return false;
-    const int32_t bt = o ? o->batch_tile : 0;
-    if (bt != 0 && bt != 16 && bt != 32 && bt != 64) return false;
-    p->batch_tile = bt;
   } else {
     if (tile == 0) tile = kGemvDefaultTile;
     if (tile < 0 || tile % kGemvGranule != 0) return false;
@@ -74,11 +88,14 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   p->variant = (fs_variant_t)variant;
   p->tile = tile;
   p->n_tiles = (V + tile - 1) / tile;
+  p->batch_tile = variant == FS_VARIANT_MFMA ? bt : 0;
+  p->tiled = layout == FS_LAYOUT_TILED;
   if (p->n_tiles > 0x7FFFFFFF) return false;
   return true;
 }
 
 hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream) {
+  if (p.tiled) return launch_stage1_tiled(a, p.variant == FS_VARIANT_MFMA, stream);
   return p.variant == FS_VARIANT_MFMA ? launch_stage1_mfma(a, stream) : launch_stage1_gemv(a, dtype, stream);
 }
 
@@ -103,9 +120,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Shared validation of the sampling entry points.
 fs_status_t check_common(const void* H, int64_t ldh, const void* W, int64_t ldw, int dtype,
                          int64_t B, int64_t D, int64_t V, float T, const void* ws,
-                         const int32_t* out) {
+                         const int32_t* out, const fs_options_t* o) {
   if (!H || !W || !ws || !out) return FS_ERR_INVALID_ARGUMENT;
   if (!sizes_ok(B, D, V)) return FS_ERR_INVALID_ARGUMENT;
+  const bool tiled = o && o->weights_layout == FS_LAYOUT_TILED;
+  if (tiled) ldw = D;  // ignored
   if (ldh < D || ldw < D) return FS_ERR_INVALID_ARGUMENT;
   if (!(T >= 0.f) || !std::isfinite(T)) return FS_ERR_INVALID_ARGUMENT;
   if (!dtype_ok(dtype)) return FS_ERR_UNSUPPORTED;
@@ -189,7 +208,7 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
                                int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
                                uint64_t step, void* workspace, size_t workspace_bytes,
                                int32_t* out_tokens, hipStream_t stream, const fs_options_t* opts) {
-  fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens);
+  fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens, opts);
   if (st != FS_OK) return st;
   Plan p;
   if (!make_plan(B, D, V, dtype, opts, &p, &st)) return st;
@@ -233,24 +252,25 @@ size_t fs_unfused_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dt
   return unfused_ws_bytes(B, V, logits_dtype);
 }
 
-fs_status_t fs_sample_unfused(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype,
-                              int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
-                              uint64_t step, fs_dtype_t logits_dtype, void* workspace,
-                              size_t workspace_bytes, int32_t* out_tokens, hipStream_t stream) {
-  fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens);
+fs_status_t fs_sample_unfused_ex(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype,
+                                 int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
+                                 uint64_t step, fs_dtype_t logits_dtype, void* workspace,
+                                 size_t workspace_bytes, int32_t* out_tokens, hipStream_t stream,
+                                 const fs_options_t* opts) {
+  fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens, opts);
   if (st != FS_OK) return st;
   if (!dtype_ok(logits_dtype)) return FS_ERR_UNSUPPORTED;
+  Plan p;
+  if (!make_plan(B, D, V, dtype, opts, &p, &st)) return st;
   if (workspace_bytes < unfused_ws_bytes(B, V, logits_dtype)) return FS_ERR_WORKSPACE_TOO_SMALL;
 
-  Plan p;
-  if (!make_plan(B, D, V, dtype, nullptr, &p, &st)) return st;
   const int64_t ld = unfused_ld(V);
   const size_t logits_bytes = align_up((size_t)B * ld * dtype_size(logits_dtype), kAlign);
   char* ws = static_cast<char*>(workspace);
   uint64_t* partial = reinterpret_cast<uint64_t*>(ws + logits_bytes);
   const int32_t n_parts = (int32_t)unfused_parts(V);
 
-  // step 1: GEMM that writes the logits
+  // step 1: GEMM that writes the logits (same Stage-1 main loop, store epilogue)
   Stage1Args a = stage1_args(H, ldh, W, ldw, B, D, V, temperature, seed, step, p);
   a.cand = nullptr;
   a.logits = ws;
@@ -265,6 +285,29 @@ fs_status_t fs_sample_unfused(const void* H, int64_t ldh, const void* W, int64_t
   e = launch_stage2(partial, a.B, n_parts, out_tokens, stream);
   if (e != hipSuccess) return fail_hip(e);
   return FS_OK;
+}
+
+fs_status_t fs_sample_unfused(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype,
+                              int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
+                              uint64_t step, fs_dtype_t logits_dtype, void* workspace,
+                              size_t workspace_bytes, int32_t* out_tokens, hipStream_t stream) {
+  return fs_sample_unfused_ex(H, ldh, W, ldw, dtype, B, D, V, temperature, seed, step, logits_dtype,
+                              workspace, workspace_bytes, out_tokens, stream, nullptr);
+}
+
+size_t fs_tiled_weights_bytes(int64_t V, int64_t D, fs_dtype_t dtype) {
+  if (dtype != FS_DTYPE_BF16 || !sizes_ok(1, D, V)) return 0;
+  return (size_t)tiled_weights_bytes(V, D);
+}
+
+fs_status_t fs_pack_weights_tiled(const void* W, int64_t ldw, int64_t V, int64_t D, fs_dtype_t dtype,
+                                  void* tiled, size_t tiled_bytes, hipStream_t stream) {
+  if (!W || !tiled || !sizes_ok(1, D, V) || ldw < D) return FS_ERR_INVALID_ARGUMENT;
+  if (!dtype_ok(dtype) || dtype != FS_DTYPE_BF16) return FS_ERR_UNSUPPORTED;
+  if (!aligned16(W) || !aligned16(tiled) || (D * 2) % 16 || (ldw * 2) % 16) return FS_ERR_UNSUPPORTED;
+  if (tiled_bytes < (size_t)tiled_weights_bytes(V, D)) return FS_ERR_WORKSPACE_TOO_SMALL;
+  hipError_t e = launch_pack_tiled(W, ldw, (int32_t)V, (int32_t)D, tiled, stream);
+  return e == hipSuccess ? FS_OK : fail_hip(e);
 }
 
 fs_status_t fs_test_philox(uint64_t seed, uint64_t step, int64_t b, int64_t v0, int64_t n,

@@ -157,6 +157,9 @@ struct Stage1Args {
 hipError_t launch_stage1_gemv(const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream);
 int gemv_batch_tile(int64_t B, int64_t D, fs_dtype_t dtype);
 hipError_t launch_stage1_mfma(const Stage1Args& a, hipStream_t stream);
+hipError_t launch_stage1_tiled(const Stage1Args& a, bool mfma, hipStream_t stream);
+hipError_t launch_pack_tiled(const void* W, int64_t ldw, int32_t V, int32_t D, void* out, hipStream_t stream);
+int64_t tiled_weights_bytes(int64_t V, int64_t D);
 int mfma_tile_rows(int blocks_per_wave);
 hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32_t* out,
                          hipStream_t stream);

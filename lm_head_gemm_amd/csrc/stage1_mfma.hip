@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void stage1_mfma_kernel(Stage1Args a, 
       uint64_t k = red[0][tid];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) k = umax64(k, red[w][tid]);
-      a.cand[(int64_t)(b0 + tid) * a.n_tiles + vt] = k;
+      a.cand[(int64_t)vt * a.B + b0 + tid] = k;
     }
   }
 }

@@ -1,0 +1,427 @@
+// Stage 1 on the tiled weight layout: FlashSampling's fused kernel (arXiv
+// 2603.15854, Section 3, "Stage 1 (Fused Kernel)") reading W from a one-time
+// repacked copy laid out for CDNA4's matrix cores.
+//
+// Tiled layout (weights are static, so the LM head is repacked once):
+//   W is cut into blocks of 16 vocab rows x 256 columns (8 KiB of bf16).
+//   Block (m, c) covers rows 16m .. 16m+15 and columns 256c .. 256c+255.
+//   Eight consecutive row blocks form a group, and a group is stored column
+//   step by column step: block (m, c) sits at block index
+//   ((m / 8) * nC + c) * 8 + m % 8   (nC = ceil(D / 256)).
+//   Inside a block, step t (0..7) holds 64 pieces of 16 bytes; piece `lane`
+//   = (r, q) = (lane % 16, lane / 16) is W[16m + r][256c + 32t + 8q .. +8],
+//   exactly the A operand of v_mfma_f32_16x16x32_bf16 for K step t. Rows past
+//   V (up to a whole group) and columns past D are zero.
+// Consequences: a wave load of one step is 1 KiB contiguous and already in
+// operand layout (no LDS transpose), and the waves of a workgroup, one row
+// block each, read adjacent blocks, so at each column step the workgroup
+// streams 32 or 64 KiB of contiguous memory: the access pattern HBM serves
+// best (measured: 86% of peak, against 75% for 16-row interleaved reads).
+//
+// Two kernels read it:
+//  * GEMV (B <= 4): each lane accumulates bf16 dot products of its row piece
+//    with H (staged once in LDS; the four lanes of a row share nothing but
+//    the reduction), then two butterfly steps finish each row's sum;
+//  * MFMA (larger B): the A operand comes straight from the loads; H chunks
+//    are staged in LDS and shared by the workgroup's waves.
+// Both end in the same register epilogue: l * (1/T) + Gumbel(Philox word),
+// packed-key maximum per batch row, one candidate per (row, vocab tile).
+#include "fs_common.h"
+
+namespace fs {
+namespace {
+
+constexpr int kBK = 256;            // columns per block
+constexpr int kKS = 8;              // K steps of 32 per block
+constexpr int kBlock16 = kKS * 64;  // 16-byte pieces per block
+constexpr int kLdsRow = kBK + 8;    // padded H row in LDS (elements)
+constexpr int kXcds = 8;
+constexpr int kGroup = 8;           // row blocks per group in the tiled layout
+
+// First 16-byte piece of block (m, c) of the tiled layout.
+__device__ __forceinline__ int64_t block_piece(int m, int c, int nC) {
+  return (((int64_t)(m / kGroup) * nC + c) * kGroup + (m % kGroup)) * kBlock16;
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float dot8_bf16(const uint4& w, const uint4& h, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, h.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, h.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, h.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, h.w), acc, false);
+  return acc;
+}
+
+// Same mapping as the row-major MFMA kernel: batch tiles of one vocab tile
+// run back to back on one XCD (workgroup i goes to XCD i mod 8).
+__device__ __forceinline__ bool tile_of(int L, int n_vt, int n_bt, int* vt, int* bt) {
+  if (n_bt == 1) {
+    *vt = L;
+    *bt = 0;
+    return L < n_vt;
+  }
+  const int G = n_vt * n_bt;
+  const int per = (G + kXcds - 1) / kXcds;
+  const int logical = (L % kXcds) * per + L / kXcds;
+  if (logical >= G) return false;
+  *vt = logical / n_bt;
+  *bt = logical - *vt * n_bt;
+  return true;
+}
+
+__device__ __forceinline__ void store_logits4(const Stage1Args& a, int b, int v0, int v_end, const float (&l)[4]) {
+  const int64_t off = (int64_t)b * a.ld_logits + v0;
+  if (a.logits_bf16) {
+    uint16_t* p = static_cast<uint16_t*>(a.logits) + off;
+    if (v0 + 3 < v_end && (off & 3) == 0) {
+      *reinterpret_cast<uint2*>(p) =
+          make_uint2((uint32_t)f32_to_bf16_rne(l[0]) | ((uint32_t)f32_to_bf16_rne(l[1]) << 16),
+                     (uint32_t)f32_to_bf16_rne(l[2]) | ((uint32_t)f32_to_bf16_rne(l[3]) << 16));
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (v0 + j < v_end) p[j] = f32_to_bf16_rne(l[j]);
+    }
+  } else {
+    float* p = static_cast<float*>(a.logits) + off;
+    if (v0 + 3 < v_end && (off & 3) == 0) {
+      *reinterpret_cast<float4*>(p) = make_float4(l[0], l[1], l[2], l[3]);
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (v0 + j < v_end) p[j] = l[j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pack
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W, int64_t ldw, int32_t V,
+                                                   int32_t D, int32_t nC, int64_t n16,
+                                                   uint4* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const int lane = (int)(i & 63);
+  const int t = (int)((i >> 6) & (kKS - 1));
+  const int64_t blk = i / kBlock16;                 // ((g * nC) + c) * 8 + m % 8
+  const int64_t g = blk / ((int64_t)kGroup * nC);
+  const int rem = (int)(blk - g * kGroup * nC);
+  const int c = rem / kGroup;
+  const int m = (int)(g * kGroup) + rem % kGroup;
+  const int row = 16 * m + (lane & 15);
+  const int k = kBK * c + 32 * t + 8 * (lane >> 4);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < V && k < D) v = *reinterpret_cast<const uint4*>(W + (int64_t)row * ldw + k);
+  out[i] = v;
+}
+
+// ---------------------------------------------------------------- GEMV
+template <int BB, int NW, bool SAMPLE, bool STORE>
+__global__ __launch_bounds__(64 * NW) void gemv_tiled_kernel(Stage1Args a) {
+  static_assert(BB == 1 || BB == 2 || BB == 4, "batch tile");
+  extern __shared__ uint4 lds_h[];          // [BB][D / 8] pieces of H
+  __shared__ uint64_t red[NW][BB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int vt = blockIdx.x;
+  const int b0 = blockIdx.y * BB;
+  const int D = a.D;
+  const int nC = (D + kBK - 1) / kBK;
+  const int nM = (a.V + 15) / 16;
+  const int d8 = D / 8;
+
+  for (int i = tid; i < BB * d8; i += 64 * NW) {
+    const int b = i / d8;
+    const int c = i - b * d8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (b0 + b < a.B)
+      v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.H) + (int64_t)(b0 + b) * a.ldh + 8 * c);
+    lds_h[i] = v;
+  }
+  __syncthreads();
+
+  const int m = vt * NW + wave;
+  const bool has_rows = m < nM;
+  const int mc = min(m, nM - 1);
+  const uint4* wt = static_cast<const uint4*>(a.W) + lane;
+
+  float acc[BB];
+#pragma unroll
+  for (int b = 0; b < BB; ++b) acc[b] = 0.f;
+
+  // two blocks (16 KiB per wave) in flight per iteration
+  for (int c0 = 0; c0 < nC; c0 += 2) {
+    uint4 w[2][kKS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < kKS; ++t) {
+        w[u][t] = make_uint4(0u, 0u, 0u, 0u);
+        if (has_rows && c0 + u < nC) w[u][t] = load_stream16(wt + block_piece(mc, c0 + u, nC) + t * 64);
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u;
+#pragma unroll
+      for (int t = 0; t < kKS; ++t) {
+        const int k8 = 32 * c + 4 * t + q;   // 16-byte piece of H this lane pairs with
+        if (c < nC && 8 * k8 < D) {
+#pragma unroll
+          for (int b = 0; b < BB; ++b) acc[b] = dot8_bf16(w[u][t], lds_h[b * d8 + k8], acc[b]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int b = 0; b < BB; ++b) {
+    acc[b] += __shfl_xor(acc[b], 16);
+    acc[b] += __shfl_xor(acc[b], 32);
+  }
+  // lane (r, q) now handles row 16m + r of batch row b0 + q
+  float l = acc[0];
+#pragma unroll
+  for (int b = 1; b < BB; ++b)
+    if (q == b) l = acc[b];
+  const int v = 16 * m + r;
+  const int batch = b0 + q;
+  const bool valid = has_rows && v < a.V && q < BB && batch < a.B;
+
+  if constexpr (STORE) {
+    if (valid) {
+      const int64_t off = (int64_t)batch * a.ld_logits + v;
+      if (a.logits_bf16) static_cast<uint16_t*>(a.logits)[off] = f32_to_bf16_rne(l);
+      else static_cast<float*>(a.logits)[off] = l;
+    }
+  }
+  if constexpr (SAMPLE) {
+    float s = l;
+    if (!a.greedy) {
+      const uint4 words = philox_quad(a.nk, (uint32_t)(v >> 2), (uint32_t)batch);
+      s = fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, r & 3)));
+    }
+    uint64_t best = valid ? pack_key(s, (uint32_t)v) : 0ull;
+#pragma unroll
+    for (int mk = 1; mk < 16; mk <<= 1) best = umax64(best, shfl_xor_u64(best, mk));
+    if (r == 0 && q < BB) red[wave][q] = best;
+    __syncthreads();
+    if (tid < BB && b0 + tid < a.B) {
+      uint64_t k = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) k = umax64(k, red[w][tid]);
+      a.cand[(int64_t)vt * a.B + b0 + tid] = k;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MFMA
+template <int NB, int NW, bool SAMPLE, bool STORE>
+__global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
+  constexpr int BN = 16 * NB;
+  constexpr int NT = 64 * NW;
+  constexpr int HP = BN * (kBK / 8) / NT;   // 16-byte pieces of H per thread per block
+  static_assert(HP >= 1 && HP * NT == BN * (kBK / 8), "batch tile vs workgroup size");
+
+  __shared__ uint4 lds_h4[2 * BN * kLdsRow / 8];
+  __shared__ uint64_t red[NW][BN];
+  uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
+
+  int vt, bt;
+  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int b0 = bt * BN;
+  const int D = a.D;
+  const int nC = (D + kBK - 1) / kBK;
+  const int nM = (a.V + 15) / 16;
+  const int m = vt * NW + wave;
+  const bool has_rows = m < nM;
+  const int mc = min(m, nM - 1);
+  const uint4* wt = static_cast<const uint4*>(a.W) + lane;
+  const uint16_t* H = static_cast<const uint16_t*>(a.H);
+
+  auto load_w = [&](int c, uint4 (&w)[kKS]) {
+    const uint4* p = wt + block_piece(mc, c, nC);
+#pragma unroll
+    for (int t = 0; t < kKS; ++t) w[t] = has_rows ? load_stream16(p + t * 64) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto load_h = [&](int c, uint4 (&h)[HP]) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      const int p = tid + NT * i;
+      const int n = p / (kBK / 8);
+      const int k = c * kBK + 8 * (p % (kBK / 8));
+      h[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (b0 + n < a.B && k < D) h[i] = *reinterpret_cast<const uint4*>(H + (int64_t)(b0 + n) * a.ldh + k);
+    }
+  };
+  auto store_h = [&](int buf, const uint4 (&h)[HP]) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      const int p = tid + NT * i;
+      *reinterpret_cast<uint4*>(lds_h + buf * BN * kLdsRow + (p / (kBK / 8)) * kLdsRow + 8 * (p % (kBK / 8))) = h[i];
+    }
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // W for block c+1 is in flight while block c is multiplied (two register
+  // sets, used alternately); H for block c+1 is loaded during block c and
+  // stored to the other LDS buffer before the workgroup barrier.
+  uint4 w[2][kKS];
+  uint4 hreg[HP];
+  load_h(0, hreg);
+  store_h(0, hreg);
+  load_w(0, w[0]);
+  __syncthreads();
+
+  for (int c0 = 0; c0 < nC; c0 += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = c0 + s;
+      if (c < nC) {
+        const bool more = c + 1 < nC;
+        if (more) {
+          load_h(c + 1, hreg);  // before W: needed first, loads complete in order
+          load_w(c + 1, w[s ^ 1]);
+        }
+        const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow;
+#pragma unroll
+        for (int t = 0; t < kKS; ++t) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
+            acc[nb] = mfma16x16x32(w[s][t], bfrag, acc[nb]);
+          }
+        }
+        if (more) store_h((c + 1) & 1, hreg);
+        __syncthreads();
+      }
+    }
+  }
+
+  const int v0 = 16 * m + 4 * q;   // this lane's four consecutive vocab rows
+  if constexpr (STORE) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int b = b0 + nb * 16 + r;
+      if (b < a.B && has_rows) {
+        const float l[4] = {acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]};
+        store_logits4(a, b, v0, a.V, l);
+      }
+    }
+  }
+  if constexpr (SAMPLE) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int b = b0 + nb * 16 + r;
+      uint4 words = make_uint4(0u, 0u, 0u, 0u);
+      if (!a.greedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float l = acc[nb][j];
+        const float s = a.greedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, j)));
+        const bool valid = has_rows && v0 + j < a.V && b < a.B;
+        best = umax64(best, valid ? pack_key(s, (uint32_t)(v0 + j)) : 0ull);
+      }
+      best = umax64(best, shfl_xor_u64(best, 16));
+      best = umax64(best, shfl_xor_u64(best, 32));
+      if (q == 0) red[wave][nb * 16 + r] = best;
+    }
+    __syncthreads();
+    if (tid < BN && b0 + tid < a.B) {
+      uint64_t k = red[0][tid];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) k = umax64(k, red[w2][tid]);
+      a.cand[(int64_t)vt * a.B + b0 + tid] = k;
+    }
+  }
+}
+
+template <int BB, int NW>
+hipError_t launch_gemv_bb(const Stage1Args& a, hipStream_t stream) {
+  const bool sample = a.cand != nullptr;
+  const bool store = a.logits != nullptr;
+  const dim3 grid(a.n_tiles, (a.B + BB - 1) / BB);
+  const size_t lds = (size_t)BB * a.D * 2;
+  void (*k)(Stage1Args) = nullptr;
+  if (sample && store) k = gemv_tiled_kernel<BB, NW, true, true>;
+  else if (sample) k = gemv_tiled_kernel<BB, NW, true, false>;
+  else k = gemv_tiled_kernel<BB, NW, false, true>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  return launch(k, grid, dim3(64 * NW), lds, stream, a);
+}
+
+template <int NW>
+hipError_t launch_gemv_nw(const Stage1Args& a, hipStream_t stream) {
+  const int bb = a.B <= 1 ? 1 : a.B <= 2 ? 2 : 4;
+  if (bb == 1) return launch_gemv_bb<1, NW>(a, stream);
+  if (bb == 2) return launch_gemv_bb<2, NW>(a, stream);
+  return launch_gemv_bb<4, NW>(a, stream);
+}
+
+template <int NB, int NW>
+hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
+  constexpr int BN = 16 * NB;
+  const bool sample = a.cand != nullptr;
+  const bool store = a.logits != nullptr;
+  const int n_bt = (a.B + BN - 1) / BN;
+  const int64_t G = (int64_t)a.n_tiles * n_bt;
+  const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  void (*k)(Stage1Args, int32_t) = nullptr;
+  if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true>;
+  else if (sample) k = mfma_tiled_kernel<NB, NW, true, false>;
+  else k = mfma_tiled_kernel<NB, NW, false, true>;
+  return launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, a, (int32_t)n_bt);
+}
+
+template <int NW>
+hipError_t launch_mfma_nw(const Stage1Args& a, hipStream_t stream) {
+  const int bn = a.batch_tile ? a.batch_tile : (a.B <= 16 ? 16 : a.B <= 32 ? 32 : 64);
+  if (bn == 16) return launch_mfma_nb<1, NW>(a, stream);
+  if (bn == 32) return launch_mfma_nb<2, NW>(a, stream);
+  return launch_mfma_nb<4, NW>(a, stream);
+}
+
+}  // namespace
+
+int64_t tiled_weights_bytes(int64_t V, int64_t D) {
+  const int64_t groups = ((V + 15) / 16 + kGroup - 1) / kGroup;
+  return groups * kGroup * ((D + kBK - 1) / kBK) * (int64_t)kBlock16 * 16;
+}
+
+hipError_t launch_pack_tiled(const void* W, int64_t ldw, int32_t V, int32_t D, void* out, hipStream_t stream) {
+  const int nC = (D + kBK - 1) / kBK;
+  const int64_t n16 = tiled_weights_bytes(V, D) / 16;
+  const dim3 grid((unsigned)((n16 + 255) / 256));
+  return launch(pack_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(W), ldw, V, D, nC, n16,
+                static_cast<uint4*>(out));
+}
+
+// Vocab tile = 16 rows per wave x waves per workgroup (4 or 8).
+hipError_t launch_stage1_tiled(const Stage1Args& a, bool mfma, hipStream_t stream) {
+  const bool eight = a.vocab_tile == 128;
+  if (mfma) return eight ? launch_mfma_nw<8>(a, stream) : launch_mfma_nw<4>(a, stream);
+  return eight ? launch_gemv_nw<8>(a, stream) : launch_gemv_nw<4>(a, stream);
+}
+
+}  // namespace fs

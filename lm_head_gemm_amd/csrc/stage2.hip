@@ -10,24 +10,23 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One workgroup of 1024 lanes per batch row; each lane folds its keys with
-// four independent loads in flight, so a row of several thousand tile
-// candidates costs about one memory round trip.
-constexpr int kS2Threads = 1024;
-
-__global__ __launch_bounds__(kS2Threads) void stage2_kernel(const uint64_t* __restrict__ cand,
-                                                            int32_t n_tiles,
-                                                            int32_t* __restrict__ out) {
-  __shared__ uint64_t red[kS2Threads / 64];
+// One workgroup per batch row; each lane folds its keys with four
+// independent loads in flight, so a row of candidates costs about one memory
+// round trip. 256 lanes cover up to 1024 tiles per round; rows with many
+// more tiles (small vocab tiles) use 1024 lanes.
+template <int NT>
+__global__ __launch_bounds__(NT) void stage2_kernel(const uint64_t* __restrict__ cand, int32_t n_tiles,
+                                                    int32_t B, int32_t* __restrict__ out) {
+  __shared__ uint64_t red[NT / 64];
   const int row = blockIdx.x;
-  const uint64_t* c = cand + (int64_t)row * n_tiles;
+  const uint64_t* c = cand + row;   // candidate of tile t at c[t * B]
   uint64_t best = 0ull;
-  for (int t0 = threadIdx.x; t0 < n_tiles; t0 += 4 * kS2Threads) {
+  for (int t0 = threadIdx.x; t0 < n_tiles; t0 += 4 * NT) {
     uint64_t k[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int t = t0 + u * kS2Threads;
-      k[u] = t < n_tiles ? c[t] : 0ull;
+      const int t = t0 + u * NT;
+      k[u] = t < n_tiles ? c[(int64_t)t * B] : 0ull;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) best = umax64(best, k[u]);
@@ -37,7 +36,7 @@ __global__ __launch_bounds__(kS2Threads) void stage2_kernel(const uint64_t* __re
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
   __syncthreads();
   if (threadIdx.x < 64) {
-    uint64_t k = threadIdx.x < kS2Threads / 64 ? red[threadIdx.x] : 0ull;
+    uint64_t k = threadIdx.x < NT / 64 ? red[threadIdx.x] : 0ull;
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) k = umax64(k, shfl_xor_u64(k, m));
     if (threadIdx.x == 0) out[row] = key_to_token(k);
@@ -46,7 +45,7 @@ __global__ __launch_bounds__(kS2Threads) void stage2_kernel(const uint64_t* __re
 
 // Gumbel-max over materialised logits: workgroup (part, row) scans `part`
 // consecutive vocab entries of one row, four at a time (one Philox call per
-// four), and writes its best key to partial[row, part].
+// four), and writes its best key to partial[part, row].
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void sample_logits_kernel(
     const void* __restrict__ logits, int64_t ld, int32_t V, float inv_t, int32_t greedy,
@@ -91,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void sample_logits_kernel(
     uint64_t k = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) k = umax64(k, red[w]);
-    partial[(int64_t)row * n_parts + blockIdx.x] = k;
+    partial[(int64_t)blockIdx.x * gridDim.y + row] = k;
   }
 }
 
@@ -152,7 +151,8 @@ hipError_t launch_probe_read(const void* src, int64_t bytes, int64_t chunk_bytes
 
 hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32_t* out,
                          hipStream_t stream) {
-  return launch(stage2_kernel, dim3(B), dim3(kS2Threads), 0, stream, cand, n_tiles, out);
+  if (n_tiles <= 4 * 256) return launch(stage2_kernel<256>, dim3(B), dim3(256), 0, stream, cand, n_tiles, B, out);
+  return launch(stage2_kernel<1024>, dim3(B), dim3(1024), 0, stream, cand, n_tiles, B, out);
 }
 
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,

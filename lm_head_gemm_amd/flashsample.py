@@ -30,6 +30,9 @@ FS_VARIANT_MFMA = 2
 
 VARIANTS = {"auto": FS_VARIANT_AUTO, "gemv": FS_VARIANT_GEMV, "mfma": FS_VARIANT_MFMA}
 
+FS_LAYOUT_ROWS = 0
+FS_LAYOUT_TILED = 1
+
 
 class FsOptions(ctypes.Structure):
     _fields_ = [
@@ -41,6 +44,8 @@ class FsOptions(ctypes.Structure):
         ("batch_tile", ctypes.c_int32),
         ("stage1_start", ctypes.c_void_p),
         ("stage1_stop", ctypes.c_void_p),
+        ("weights_layout", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -77,9 +82,16 @@ def _load():
     lib.fs_sample_fused_ex.argtypes = fused + [ctypes.POINTER(FsOptions)]
     lib.fs_unfused_workspace_bytes.restype = c_sz
     lib.fs_unfused_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int]
+    unfused = [vp, c_i64, vp, c_i64, ctypes.c_int, c_i64, c_i64, c_i64, ctypes.c_float, c_u64, c_u64,
+               ctypes.c_int, vp, c_sz, vp, vp]
     lib.fs_sample_unfused.restype = ctypes.c_int
-    lib.fs_sample_unfused.argtypes = [vp, c_i64, vp, c_i64, ctypes.c_int, c_i64, c_i64, c_i64,
-                                      ctypes.c_float, c_u64, c_u64, ctypes.c_int, vp, c_sz, vp, vp]
+    lib.fs_sample_unfused.argtypes = unfused
+    lib.fs_sample_unfused_ex.restype = ctypes.c_int
+    lib.fs_sample_unfused_ex.argtypes = unfused + [ctypes.POINTER(FsOptions)]
+    lib.fs_tiled_weights_bytes.restype = c_sz
+    lib.fs_tiled_weights_bytes.argtypes = [c_i64, c_i64, ctypes.c_int]
+    lib.fs_pack_weights_tiled.restype = ctypes.c_int
+    lib.fs_pack_weights_tiled.argtypes = [vp, c_i64, c_i64, c_i64, ctypes.c_int, vp, c_sz, vp]
     lib.fs_test_philox.restype = ctypes.c_int
     lib.fs_test_philox.argtypes = [c_u64, c_u64, c_i64, c_i64, c_i64, vp, vp]
     lib.fs_test_gumbel.restype = ctypes.c_int
@@ -112,22 +124,53 @@ def _check(st: int, where: str):
         raise FlashSampleError(st, where)
 
 
-def _check_inputs(H: torch.Tensor, W: torch.Tensor):
-    if not (H.is_cuda and W.is_cuda):
+class TiledWeights:
+    """A bf16 LM head [V, D] repacked once into the tiled layout
+    (fs_pack_weights_tiled): blocks of 16 vocab rows x 256 columns, each 8 KiB
+    contiguous in matrix-core operand order. Pass it wherever W is taken."""
+
+    def __init__(self, W: torch.Tensor, stream=None):
+        if not W.is_cuda or W.dtype != torch.bfloat16 or W.dim() != 2 or W.stride(1) != 1:
+            raise ValueError("TiledWeights needs a bf16 device tensor [V, D] with contiguous rows")
+        self.V, self.D = W.shape
+        nbytes = int(_lib.fs_tiled_weights_bytes(self.V, self.D, FS_DTYPE_BF16))
+        self.data = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+        _check(_lib.fs_pack_weights_tiled(W.data_ptr(), W.stride(0), self.V, self.D, FS_DTYPE_BF16,
+                                          self.data.data_ptr(), nbytes, _stream(stream)),
+               "fs_pack_weights_tiled")
+        self.dtype = W.dtype
+        self.device = W.device
+
+    @property
+    def shape(self):
+        return (self.V, self.D)
+
+
+def _weights(W):
+    """(pointer, ldw, V, D, layout) of a row-major tensor or TiledWeights."""
+    if isinstance(W, TiledWeights):
+        return W.data.data_ptr(), W.D, W.V, W.D, FS_LAYOUT_TILED
+    return W.data_ptr(), W.stride(0), W.shape[0], W.shape[1], FS_LAYOUT_ROWS
+
+
+def _check_inputs(H: torch.Tensor, W):
+    if not (H.is_cuda and W.device.type == "cuda"):
         raise ValueError("H and W must be device tensors")
-    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+    if H.dim() != 2 or len(W.shape) != 2 or H.shape[1] != W.shape[1]:
         raise ValueError(f"H [B, D] and W [V, D] expected, got {tuple(H.shape)} and {tuple(W.shape)}")
     if H.dtype != W.dtype:
         raise ValueError("H and W must share a dtype")
-    if H.stride(1) != 1 or W.stride(1) != 1:
+    if H.stride(1) != 1 or (isinstance(W, torch.Tensor) and W.stride(1) != 1):
         raise ValueError("H and W rows must be contiguous")
 
 
-def make_options(variant="auto", vocab_tile=0, logits=None, events=None, batch_tile=0) -> FsOptions:
+def make_options(variant="auto", vocab_tile=0, logits=None, events=None, batch_tile=0,
+                 layout=FS_LAYOUT_ROWS) -> FsOptions:
     o = FsOptions()
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     o.vocab_tile = int(vocab_tile)
     o.batch_tile = int(batch_tile)
+    o.weights_layout = int(layout)
     if logits is not None:
         o.logits = logits.data_ptr()
         o.ld_logits = logits.stride(0)
@@ -138,13 +181,13 @@ def make_options(variant="auto", vocab_tile=0, logits=None, events=None, batch_t
     return o
 
 
-def num_vocab_tiles(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0) -> int:
-    o = make_options(variant, vocab_tile)
+def num_vocab_tiles(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0, tiled=False) -> int:
+    o = make_options(variant, vocab_tile, layout=FS_LAYOUT_TILED if tiled else FS_LAYOUT_ROWS)
     return int(_lib.fs_num_vocab_tiles(B, D, V, _dtype_code(dtype), ctypes.byref(o)))
 
 
-def workspace_bytes(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0) -> int:
-    o = make_options(variant, vocab_tile)
+def workspace_bytes(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0, tiled=False) -> int:
+    o = make_options(variant, vocab_tile, layout=FS_LAYOUT_TILED if tiled else FS_LAYOUT_ROWS)
     return int(_lib.fs_workspace_bytes_ex(B, D, V, _dtype_code(dtype), ctypes.byref(o)))
 
 
@@ -152,45 +195,47 @@ def unfused_workspace_bytes(B, D, V, dtype=torch.bfloat16, logits_dtype=torch.bf
     return int(_lib.fs_unfused_workspace_bytes(B, D, V, _dtype_code(dtype), _dtype_code(logits_dtype)))
 
 
-def sample_fused(H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
+def sample_fused(H: torch.Tensor, W, temperature: float, seed: int, step: int,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                  variant="auto", vocab_tile: int = 0, logits: torch.Tensor | None = None,
                  events=None, stream=None, batch_tile: int = 0) -> torch.Tensor:
-    """One token per row of H from softmax(H W^T / T) (Gumbel-max, fused)."""
+    """One token per row of H from softmax(H W^T / T) (Gumbel-max, fused).
+    W is a row-major [V, D] tensor or a TiledWeights."""
     _check_inputs(H, W)
     B, D = H.shape
-    V = W.shape[0]
-    o = make_options(variant, vocab_tile, logits, events, batch_tile)
+    wptr, ldw, V, _, layout = _weights(W)
+    o = make_options(variant, vocab_tile, logits, events, batch_tile, layout)
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=H.device)
     if workspace is None:
         nbytes = int(_lib.fs_workspace_bytes_ex(B, D, V, _dtype_code(H.dtype), ctypes.byref(o)))
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=H.device)
-    st = _lib.fs_sample_fused_ex(H.data_ptr(), H.stride(0), W.data_ptr(), W.stride(0),
-                                 _dtype_code(H.dtype), B, D, V, float(temperature), int(seed),
-                                 int(step), workspace.data_ptr(), workspace.numel(),
-                                 out.data_ptr(), _stream(stream), ctypes.byref(o))
+    st = _lib.fs_sample_fused_ex(H.data_ptr(), H.stride(0), wptr, ldw, _dtype_code(H.dtype), B, D, V,
+                                 float(temperature), int(seed), int(step), workspace.data_ptr(),
+                                 workspace.numel(), out.data_ptr(), _stream(stream), ctypes.byref(o))
     _check(st, "fs_sample_fused_ex")
     return out
 
 
-def sample_unfused(H: torch.Tensor, W: torch.Tensor, temperature: float, seed: int, step: int,
+def sample_unfused(H: torch.Tensor, W, temperature: float, seed: int, step: int,
                    logits_dtype=torch.bfloat16, out: torch.Tensor | None = None,
-                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                   workspace: torch.Tensor | None = None, stream=None, variant="auto",
+                   vocab_tile: int = 0, batch_tile: int = 0) -> torch.Tensor:
     """The IO-model baseline: GEMM writes logits, a sampler kernel reads them."""
     _check_inputs(H, W)
     B, D = H.shape
-    V = W.shape[0]
+    wptr, ldw, V, _, layout = _weights(W)
+    o = make_options(variant, vocab_tile, None, None, batch_tile, layout)
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=H.device)
     if workspace is None:
         nbytes = unfused_workspace_bytes(B, D, V, H.dtype, logits_dtype)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=H.device)
-    st = _lib.fs_sample_unfused(H.data_ptr(), H.stride(0), W.data_ptr(), W.stride(0),
-                                _dtype_code(H.dtype), B, D, V, float(temperature), int(seed), int(step),
-                                _dtype_code(logits_dtype), workspace.data_ptr(), workspace.numel(),
-                                out.data_ptr(), _stream(stream))
-    _check(st, "fs_sample_unfused")
+    st = _lib.fs_sample_unfused_ex(H.data_ptr(), H.stride(0), wptr, ldw, _dtype_code(H.dtype), B, D, V,
+                                   float(temperature), int(seed), int(step), _dtype_code(logits_dtype),
+                                   workspace.data_ptr(), workspace.numel(), out.data_ptr(), _stream(stream),
+                                   ctypes.byref(o))
+    _check(st, "fs_sample_unfused_ex")
     return out
 
 

@@ -143,3 +143,37 @@ def test_test_hooks_validation(lib):
     assert lib.fs_test_philox(0, 0, 0, 0, 4, None, None) == INVALID
     assert lib.fs_test_gumbel(None, 4, FAKE, None) == INVALID
     assert lib.fs_test_gumbel(FAKE, 0, FAKE, None) == INVALID
+
+
+def test_tiled_layout_validation(lib):
+    from lm_head_gemm_amd.flashsample import FsOptions
+    assert lib.fs_tiled_weights_bytes(4099, 1032, BF16) == 264 * 5 * 8192   # 257 blocks -> 33 groups of 8
+    assert lib.fs_tiled_weights_bytes(16, 256, BF16) == 8 * 8192
+    assert lib.fs_tiled_weights_bytes(16, 256, F32) == 0
+    assert lib.fs_tiled_weights_bytes(0, 256, BF16) == 0
+    assert lib.fs_pack_weights_tiled(None, 64, 10, 64, BF16, FAKE, 1 << 20, None) == INVALID
+    assert lib.fs_pack_weights_tiled(FAKE, 32, 10, 64, BF16, FAKE, 1 << 20, None) == INVALID
+    assert lib.fs_pack_weights_tiled(FAKE, 64, 10, 64, F32, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.fs_pack_weights_tiled(FAKE, 64, 10, 64, BF16, FAKE + 8, 1 << 20, None) == UNSUPPORTED
+    assert lib.fs_pack_weights_tiled(FAKE, 64, 10, 64, BF16, FAKE, 100, None) == WS_SMALL
+    o = FsOptions()
+    o.weights_layout = 2
+    assert _fused(lib, opts=o) == INVALID
+    o = FsOptions()
+    o.reserved = 1
+    assert _fused(lib, opts=o) == INVALID
+    o = FsOptions()
+    o.weights_layout = 1
+    assert _fused(lib, opts=o, dtype=F32) == UNSUPPORTED
+    o.vocab_tile = 96
+    assert _fused(lib, opts=o) == INVALID
+    o.vocab_tile = 128
+    o.batch_tile = 48
+    assert _fused(lib, opts=o) == INVALID
+    # ldw is ignored for the tiled layout; the other checks still apply
+    o.batch_tile = 0
+    assert _fused(lib, opts=o, ldw=0, wsb=8) == WS_SMALL
+    base = [FAKE, 64, FAKE, 64, BF16, 2, 64, 1000, 1.0, 0, 0, F32, FAKE, 1 << 20, FAKE, None]
+    o = FsOptions()
+    o.weights_layout = 3
+    assert lib.fs_sample_unfused_ex(*base, ctypes.byref(o)) == INVALID

@@ -115,6 +115,70 @@ def test_mfma_store_logits_matches_exact(fs):
     assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - exact)) < 1e-4
 
 
+def _numpy_tiled(W):
+    """The tiled layout written out from its definition: block (m, c) of 16
+    rows x 256 columns at block index ((m // 8) * nC + c) * 8 + m % 8; inside
+    it step t, piece lane = (r, q) = (lane % 16, lane // 16) holds
+    W[16m + r, 256c + 32t + 8q : +8]; zero past V (to a whole group of 8
+    blocks) and past D."""
+    V, D = W.shape
+    nM, nC = -(-V // 16), -(-D // 256)
+    nG = -(-nM // 8)
+    P = np.zeros((nG * 8 * 16, nC * 256), dtype=W.dtype)
+    P[:V, :D] = W
+    # blocks[m, c, t, lane, 8]
+    blocks = np.empty((nG * 8, nC, 8, 64, 8), dtype=W.dtype)
+    for lane in range(64):
+        r, q = lane % 16, lane // 16
+        for t in range(8):
+            cols = np.arange(nC)[:, None] * 256 + 32 * t + 8 * q + np.arange(8)[None, :]
+            blocks[:, :, t, lane, :] = P.reshape(nG * 8, 16, -1)[:, r, :][:, cols]
+    out = blocks.reshape(nG, 8, nC, 8, 64, 8).transpose(0, 2, 1, 3, 4, 5)
+    return np.ascontiguousarray(out).reshape(-1)
+
+
+@pytest.mark.parametrize("V,D", [(1, 8), (17, 264), (1000, 512), (4099, 1032)])
+def test_pack_weights_tiled_layout(fs, V, D):
+    import torch
+    _, W = _rand_head(V + D, 1, D, V)
+    tw = fs.TiledWeights(to_device(W))
+    got = tw.data.cpu().numpy().view(np.uint16)
+    want = _numpy_tiled(W)
+    assert got.shape == want.shape and np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("variant,tile", [("auto", 0), ("gemv", 64), ("gemv", 128), ("mfma", 64), ("mfma", 128)])
+@pytest.mark.parametrize("B,D,V", [
+    (1, 64, 5), (2, 520, 2001), (3, 256, 777), (4, 1032, 3000), (16, 256, 4099),
+    (33, 4096, 2053), (64, 264, 1500), (100, 512, 1000),
+])
+def test_tiled_layout_parity(fs, variant, tile, B, D, V):
+    H, W = _rand_head(B * 11 + D + V, B, D, V)
+    Hd = to_device(H)
+    tw = fs.TiledWeights(to_device(W))
+    for T, seed, step in ((1.0, 0, 0), (0.6, 77, 2**32 + 1), (0.0, 0, 0)):
+        tok = fs.sample_fused(Hd, tw, T, seed, step, variant=variant, vocab_tile=tile).cpu().numpy()
+        check_parity(H, W, T, seed, step, np.arange(B), tok)
+
+
+def test_tiled_unfused_and_store(fs):
+    import torch
+    B, D, V = 37, 1032, 2001
+    H, W = _rand_head(21, B, D, V)
+    Hd = to_device(H)
+    tw = fs.TiledWeights(to_device(W))
+    exact = oracle.exact_logits(H, W)
+    l32 = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda")
+    tok = fs.sample_fused(Hd, tw, 1.0, 4, 4, logits=l32).cpu().numpy()
+    assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - exact)) < 1e-4
+    check_parity(H, W, 1.0, 4, 4, np.arange(B), tok)
+    for var in ("gemv", "mfma"):
+        tok = fs.sample_unfused(Hd[:3] if var == "gemv" else Hd, tw, 1.0, 4, 4, logits_dtype=torch.float32,
+                                variant=var).cpu().numpy()
+        rows = np.arange(3 if var == "gemv" else B)
+        check_parity(H[rows], W, 1.0, 4, 4, rows, tok)
+
+
 def test_batch_prefix_and_repeat_determinism(fs):
     B, D, V = 13, 256, 3001
     H, W = _rand_head(9, B, D, V)
