@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "gemv", "mfma"])
     ap.add_argument("--vocab-tile", type=int, default=0)
     ap.add_argument("--batch-tile", type=int, default=0)
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="override the workload's temperature (0 = greedy, no noise)")
     ap.add_argument("--layout", default="tiled", choices=["rows", "tiled"],
                     help="W row-major, or repacked once into the tiled matrix-core layout")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -195,6 +197,9 @@ def main():
         return
 
     wl = inputs.WORKLOADS[args.workload]
+    if args.temperature is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, temperature=args.temperature)
     B = args.batch
     log(f"[bench] generating {wl.name}: D={wl.D} V={wl.V} {wl.dtype}, B={B}")
     t = time.perf_counter()

@@ -56,21 +56,29 @@ __device__ __forceinline__ uint32_t pick_word(const uint4& w, int j) {
 }
 
 // Standard Gumbel from a 32-bit word: u = (x + 1/2) 2^-32, g = -ln(-ln u).
-// For u <= 1/2, -ln u is taken directly; for u > 1/2 it is -log1p(-(1 - u))
-// with 1 - u = (~x + 1/2) 2^-32 formed from the integer, so the small
-// argument keeps full relative precision where the largest Gumbels live.
+// Both logarithms use the hardware base-2 logarithm (v_log_f32) scaled by
+// ln 2. The inner one, e = -ln u, is taken two ways:
+//  * u <= 1/2 (x < 2^31): directly, from u formed with one rounding;
+//  * u >  1/2: from c = 1 - u = (~x + 1/2) 2^-32, formed from the integer
+//    (the largest Gumbels live here, where u itself cannot resolve them),
+//    with Goldberg's log1p correction: for w = fl(1 - c), w - 1 is exact and
+//    ln(1 - c) = ln(w) * (-c) / (w - 1) to within a few ulps
+//    (D. Goldberg, "What every computer scientist should know about
+//    floating-point arithmetic", 1991, the log(1 + x) theorem); w == 1 only
+//    when c < 2^-25, where ln(1 - c) = -c to fp32 precision.
 // Each uniform carries one fp32 rounding (relative 2^-24), which moves g by
-// at most ~1e-7 plus the fp32 rounding of g itself.
+// about 1e-7; the bound checked against the fp64 definition is 1e-5.
 __device__ __forceinline__ float gumbel_from_word(uint32_t x) {
-  float e;
-  if (x < 0x80000000u) {
-    const float u = fmaf((float)x, 0x1p-32f, 0x1p-33f);
-    e = -logf(u);
-  } else {
-    const float c = fmaf((float)(~x), 0x1p-32f, 0x1p-33f);
-    e = -log1pf(-c);
-  }
-  return -logf(e);
+  constexpr float kLn2 = 0.693147180559945309f;
+  const bool low = x < 0x80000000u;
+  const float u = fmaf((float)x, 0x1p-32f, 0x1p-33f);
+  const float c = fmaf((float)(~x), 0x1p-32f, 0x1p-33f);
+  const float w = 1.0f - c;
+  const float arg = low ? u : w;
+  const float scale = low ? 1.0f : c * __builtin_amdgcn_rcpf(1.0f - w);
+  float e = -kLn2 * __builtin_amdgcn_logf(arg) * scale;
+  if (!low && w == 1.0f) e = c;
+  return -kLn2 * __builtin_amdgcn_logf(e);
 }
 
 // ------------------------------------------------------------------ candidate keys
