@@ -56,8 +56,24 @@ def stage1_bytes(B, D, V, esz, n_tiles) -> int:
     return V * D * esz + B * D * esz + 8 * B * n_tiles
 
 
-def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, batch_tile=0):
-    """Returns (ms per step, mean Stage-1 ms).
+def warm(fn, warmup, min_ms):
+    """Runs fn(i) for `warmup` untimed steps and, further, until at least
+    min_ms of wall time has passed (clocks settle after tens of ms of load)."""
+    import torch
+    i = 0
+    t0 = time.perf_counter()
+    while i < warmup or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn(i)
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
+def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, batch_tile=0,
+               single_pass=False, min_warm_ms=0.0):
+    """Returns (ms per step, mean Stage-1 ms, warm-up steps run).
 
     The step time comes from `steps` back-to-back calls bracketed by two
     events; the Stage-1 time from a second pass of `steps` calls in which the
@@ -67,11 +83,13 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
     T, seed = wl.temperature, wl.seed
     tiled = isinstance(Ws[0], fs.TiledWeights)
     ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, variant=variant, vocab_tile=vocab_tile,
-                                        tiled=tiled), dtype=torch.uint8, device="cuda")
+                                        tiled=tiled, single_pass=single_pass), dtype=torch.uint8, device="cuda")
+    if single_pass:
+        fs.workspace_reset(ws)
     out = torch.empty(B, dtype=torch.int32, device="cuda")
-    kw = dict(out=out, workspace=ws, variant=variant, vocab_tile=vocab_tile, batch_tile=batch_tile)
-    for i in range(warmup):
-        fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw)
+    kw = dict(out=out, workspace=ws, variant=variant, vocab_tile=vocab_tile, batch_tile=batch_tile,
+              single_pass=single_pass)
+    n_warm = warm(lambda i: fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw), warmup, min_warm_ms)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -91,16 +109,16 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
         fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, events=ev[i], **kw)
     torch.cuda.synchronize()
     s1 = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    return total_ms / steps, s1
+    return total_ms / steps, s1, n_warm
 
 
-def time_unfused(fs, Hb, Ws, wl, steps, warmup, B, logits_dtype):
+def time_unfused(fs, Hb, Ws, wl, steps, warmup, B, logits_dtype, min_warm_ms=0.0):
     import torch
     ws = torch.empty(fs.unfused_workspace_bytes(B, wl.D, wl.V, Hb.dtype, logits_dtype), dtype=torch.uint8,
                      device="cuda")
     out = torch.empty(B, dtype=torch.int32, device="cuda")
-    for i in range(warmup):
-        fs.sample_unfused(Hb, Ws[i % len(Ws)], wl.temperature, wl.seed, i, logits_dtype, out=out, workspace=ws)
+    warm(lambda i: fs.sample_unfused(Hb, Ws[i % len(Ws)], wl.temperature, wl.seed, i, logits_dtype, out=out,
+                                     workspace=ws), warmup, min_warm_ms)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -172,6 +190,10 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="also stream W once per step with the read probe (attainable bandwidth)")
     ap.add_argument("--no-rows", action="store_true", help="skip timing the row-major layout beside")
+    ap.add_argument("--single-pass", action="store_true",
+                    help="time the one-launch form (Stage 2 folded into Stage 1) as the headline")
+    ap.add_argument("--min-warmup-ms", type=float, default=300.0,
+                    help="keep warming up (untimed) until this much wall time has passed")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -213,19 +235,23 @@ def main():
     Ws = [upload(W), upload(W)]
     esz = 2 if wl.dtype == "bf16" else 4
 
-    def run(b, weights=None):
+    single = args.single_pass
+
+    def run(b, weights=None, single_pass=None):
         weights = Ws if weights is None else weights
+        single_pass = single if single_pass is None else single_pass
         Hb = Hd[:b]
-        ms, s1 = time_fused(fs, Hb, weights, wl, args.steps, args.warmup, b, args.variant, args.vocab_tile,
-                            args.batch_tile)
+        ms, s1, n_warm = time_fused(fs, Hb, weights, wl, args.steps, args.warmup, b, args.variant,
+                                    args.vocab_tile, args.batch_tile, single_pass, args.min_warmup_ms)
         tiled = isinstance(weights[0], fs.TiledWeights)
         nt = fs.num_vocab_tiles(b, wl.D, wl.V, Hb.dtype, args.variant, args.vocab_tile, tiled=tiled)
         byts = stage1_bytes(b, wl.D, wl.V, esz, nt)
         rec = {"B": b, "ms_per_step": ms, "samples_per_s": b / (ms * 1e-3), "stage1_ms": s1,
                "stage1_GBps": byts / (s1 * 1e-3) / 1e9, "stage1_bytes": byts, "n_tiles": nt,
-               "flops": 2 * b * wl.V * wl.D}
+               "flops": 2 * b * wl.V * wl.D, "warmup_steps_run": n_warm}
         if not args.no_unfused:
-            u16 = time_unfused(fs, Hb, weights, wl, args.steps, args.warmup, b, torch.bfloat16)
+            u16 = time_unfused(fs, Hb, weights, wl, args.steps, args.warmup, b, torch.bfloat16,
+                               args.min_warmup_ms)
             rec["unfused_bf16_ms_per_step"] = u16
             rec["fused_speedup_vs_unfused_bf16"] = u16 / ms
         log(f"[bench] B={b}: {ms * 1e3:.1f} us/step, stage1 {s1 * 1e3:.1f} us "
@@ -254,6 +280,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": head["warmup_steps_run"],
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -261,15 +288,20 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded Gaussian head, FS-DATA-1)",
         "config": {"workload": wl.name, "B": B, "D": wl.D, "V": wl.V, "temperature": wl.temperature,
-                   "weights_layout": args.layout, "vocab_tiles": head["n_tiles"], "W_copies_alternated": 2},
+                   "weights_layout": args.layout, "stage2": "folded into stage 1" if single else "separate kernel",
+                   "vocab_tiles": head["n_tiles"], "W_copies_alternated": 2},
         "roofline": {"bound": "hbm", "achieved": head["stage1_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": head["stage1_GBps"] / HBM_PEAK_GBS,
                      "traffic": traffic_record("stage1", wl.name, B),
                      "kernel": "stage1 (fused GEMM + Gumbel-max epilogue)",
                      "stage1_us": head["stage1_ms"] * 1e3},
     }
+    other = run(B, single_pass=not single)
+    result["single_pass" if not single else "two_stage"] = {
+        "ms_per_step": other["ms_per_step"], "samples_per_s": other["samples_per_s"],
+        "stage1_us": other["stage1_ms"] * 1e3}
     if args.layout == "tiled" and Ws_rows is not None:
-        rows = run(B, Ws_rows)
+        rows = run(B, Ws_rows, single_pass=False)
         result["rows_layout"] = {"ms_per_step": rows["ms_per_step"], "samples_per_s": rows["samples_per_s"],
                                  "stage1_us": rows["stage1_ms"] * 1e3, "stage1_GBps": rows["stage1_GBps"]}
     if args.probe:

@@ -86,7 +86,16 @@ typedef struct fs_options {
   hipEvent_t stage1_start; /* non-null: recorded on `stream` right before and */
   hipEvent_t stage1_stop;  /* right after the Stage-1 launch (for timing) */
   int32_t weights_layout;  /* fs_layout_t of W */
-  int32_t reserved;        /* must be 0 */
+  int32_t single_pass;     /* nonzero: fold Stage 2 into Stage 1 (one launch).
+                              Each Stage-1 workgroup takes an atomic maximum
+                              of its keys into a [B] key array in the
+                              workspace; the last workgroup to finish writes
+                              the tokens and returns the workspace to zero.
+                              The workspace (fs_workspace_bytes_ex with this
+                              option) must be zero before its first use
+                              (fs_workspace_reset), and calls sharing it must
+                              not overlap. Results equal the two-stage ones. */
+  int32_t reserved[2];     /* must be 0 */
 } fs_options_t;
 
 /* Human-readable name of a status code (static storage). */
@@ -107,10 +116,16 @@ int64_t fs_num_vocab_tiles(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
 int32_t fs_vocab_tile_granule(fs_variant_t variant);
 
 /* Workspace bytes fs_sample_fused needs (candidate buffer of the Stage-1
- * tiles: one 64-bit key per (row, vocab tile)). 0 on invalid sizes. */
+ * tiles: one 64-bit key per (row, vocab tile); with single_pass, B keys and
+ * a counter). 0 on invalid sizes. */
 size_t fs_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype);
 size_t fs_workspace_bytes_ex(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
                              const fs_options_t* opts);
+
+/* Zeroes a workspace on `stream` with a fill kernel (no memset node, so it
+ * may be captured in a graph). Needed once before the first single-pass
+ * call on a workspace. bytes must be a multiple of 8; ws 16-byte aligned. */
+fs_status_t fs_workspace_reset(void* workspace, size_t bytes, hipStream_t stream);
 
 /* Fused sampler (FlashSampling Stage 1 + Stage 2; Section 3, the two-stage
  * list and the exactness paragraph).

@@ -46,6 +46,7 @@ struct Plan {
   int64_t n_tiles;
   int32_t batch_tile = 0;
   bool tiled = false;     // W in the tiled layout
+  bool single_pass = false;
 };
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
@@ -59,7 +60,7 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   *why = FS_ERR_INVALID_ARGUMENT;
   const int layout = o ? o->weights_layout : FS_LAYOUT_ROWS;
   if (layout != FS_LAYOUT_ROWS && layout != FS_LAYOUT_TILED) return false;
-  if (o && o->reserved != 0) return false;
+  if (o && (o->reserved[0] != 0 || o->reserved[1] != 0)) return false;
   int variant = o ? o->variant : FS_VARIANT_AUTO;
   if (variant != FS_VARIANT_AUTO && variant != FS_VARIANT_GEMV && variant != FS_VARIANT_MFMA) return false;
   if (variant == FS_VARIANT_AUTO)
@@ -90,6 +91,7 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   p->n_tiles = (V + tile - 1) / tile;
   p->batch_tile = variant == FS_VARIANT_MFMA ? bt : 0;
   p->tiled = layout == FS_LAYOUT_TILED;
+  p->single_pass = o && o->single_pass;
   if (p->n_tiles > 0x7FFFFFFF) return false;
   return true;
 }
@@ -100,6 +102,7 @@ hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, h
 }
 
 size_t fused_ws_bytes(int64_t B, const Plan& p) {
+  if (p.single_pass) return align_up((size_t)B * sizeof(uint64_t), kAlign) + kAlign;  // keys + counter
   return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign);
 }
 
@@ -221,6 +224,13 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
 
   Stage1Args a = stage1_args(H, ldh, W, ldw, B, D, V, temperature, seed, step, p);
   a.cand = static_cast<uint64_t*>(workspace);
+  if (p.single_pass) {
+    a.single_pass = 1;
+    a.keys = static_cast<uint64_t*>(workspace);
+    a.counter = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                            align_up((size_t)B * sizeof(uint64_t), kAlign));
+    a.out = out_tokens;
+  }
   if (opts && opts->logits) {
     a.logits = opts->logits;
     a.ld_logits = opts->ld_logits;
@@ -233,8 +243,10 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
   if (e != hipSuccess) return fail_hip(e);
   if (opts && opts->stage1_stop && (e = hipEventRecord(opts->stage1_stop, stream)) != hipSuccess)
     return fail_hip(e);
-  e = launch_stage2(a.cand, a.B, a.n_tiles, out_tokens, stream);
-  if (e != hipSuccess) return fail_hip(e);
+  if (!p.single_pass) {
+    e = launch_stage2(a.cand, a.B, a.n_tiles, out_tokens, stream);
+    if (e != hipSuccess) return fail_hip(e);
+  }
   return FS_OK;
 }
 
@@ -321,6 +333,13 @@ fs_status_t fs_test_philox(uint64_t seed, uint64_t step, int64_t b, int64_t v0, 
 fs_status_t fs_test_gumbel(const uint32_t* words, int64_t n, float* g_out, hipStream_t stream) {
   if (!words || !g_out || n <= 0 || n > ((int64_t)1 << 32)) return FS_ERR_INVALID_ARGUMENT;
   hipError_t e = launch_test_gumbel(words, n, g_out, stream);
+  return e == hipSuccess ? FS_OK : fail_hip(e);
+}
+
+fs_status_t fs_workspace_reset(void* workspace, size_t bytes, hipStream_t stream) {
+  if (!workspace || bytes == 0 || bytes % 8) return FS_ERR_INVALID_ARGUMENT;
+  if (!aligned16(workspace)) return FS_ERR_UNSUPPORTED;
+  hipError_t e = launch_fill_zero(static_cast<uint64_t*>(workspace), (int64_t)(bytes / 8), stream);
   return e == hipSuccess ? FS_OK : fail_hip(e);
 }
 

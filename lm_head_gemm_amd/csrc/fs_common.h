@@ -159,7 +159,55 @@ struct Stage1Args {
   void* logits;         // [B, V] logits, or null
   int64_t ld_logits;
   int32_t logits_bf16;  // stored logits dtype
+  // single-pass mode: Stage 2 folded into Stage 1
+  int32_t single_pass;
+  int32_t total_wgs;    // workgroups that publish candidates (set by the launcher)
+  uint64_t* keys;       // [B] running maximum keys, zero between calls
+  uint32_t* counter;    // finished workgroups, zero between calls
+  int32_t* out;         // [B] tokens
 };
+
+// Publishes one workgroup's best key per batch row (k is meaningful for
+// tid < n_rows, rows b0 .. b0 + n_rows - 1; every thread of the workgroup
+// must call this).
+//  * Two-stage mode: candidate buffer [n_tiles, B], reduced by Stage 2.
+//  * Single-pass mode (Stage 2 folded in): a device-scope atomic 64-bit
+//    maximum into keys[b]; after its maxima have completed, the workgroup
+//    counts itself finished with a device-scope atomic increment, and the
+//    one that finishes last decodes keys into tokens and returns keys and
+//    counter to zero for the next call. Every access to keys and counter is
+//    an atomic read-modify-write, performed where all XCDs see it, and each
+//    workgroup's maxima complete before its increment is issued, so the last
+//    workgroup's exchanges observe every maximum; no cache-flushing fence is
+//    needed. The maximum is order independent: results equal the two-stage
+//    ones.
+__device__ __forceinline__ void publish_candidates(const Stage1Args& a, int tile, int b0, int n_rows,
+                                                   uint64_t k, int tid, int nthreads) {
+  if (!a.single_pass) {
+    if (tid < n_rows) a.cand[(int64_t)tile * a.B + b0 + tid] = k;
+    return;
+  }
+  __shared__ int is_last;
+  uint64_t prev = 0ull;
+  if (tid < n_rows && k != 0ull)
+    prev = __hip_atomic_fetch_max(reinterpret_cast<unsigned long long*>(a.keys + b0 + tid), k,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);  // the maxima have been performed
+  (void)prev;
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)(a.total_wgs - 1);
+  __syncthreads();
+  if (is_last) {
+    for (int b = tid; b < a.B; b += nthreads) {
+      const uint64_t key = __hip_atomic_exchange(reinterpret_cast<unsigned long long*>(a.keys + b), 0ull,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.out[b] = key_to_token(key);
+    }
+    if (tid == 0) __hip_atomic_exchange(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
 // Launchers (each returns the hipError_t of its launches).
 hipError_t launch_stage1_gemv(const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream);
@@ -178,6 +226,7 @@ hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_b
 hipError_t launch_test_philox(NoiseKey nk, uint32_t b, int64_t v0, int64_t n, uint32_t* out,
                               hipStream_t stream);
 hipError_t launch_test_gumbel(const uint32_t* words, int64_t n, float* out, hipStream_t stream);
+hipError_t launch_fill_zero(uint64_t* p, int64_t n, hipStream_t stream);
 hipError_t launch_probe_read(const void* src, int64_t bytes, int64_t chunk_bytes, uint32_t* sink,
                              hipStream_t stream);
 

@@ -216,12 +216,13 @@ __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
     best = umax64(best, shfl_xor_u64(best, 2 << S));
     if ((lane & ((4 << S) - 1)) == 0) red[wave][lane >> (S + 2)] = best;
     __syncthreads();
-    if (tid < BB && b0 + tid < a.B) {
-      uint64_t k = red[0][tid];
+    uint64_t k = 0ull;
+    if (tid < BB) {
+      k = red[0][tid];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) k = umax64(k, red[w][tid]);
-      a.cand[(int64_t)tile * a.B + b0 + tid] = k;
     }
+    publish_candidates(a, tile, b0, min(BB, a.B - b0), k, tid, kThreads);
   }
 }
 
@@ -239,7 +240,9 @@ hipError_t launch_bb(const Stage1Args& a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  return launch(k, grid, dim3(kThreads), lds, stream, a);
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)(grid.x * grid.y);
+  return launch(k, grid, dim3(kThreads), lds, stream, b);
 }
 
 }  // namespace

@@ -249,12 +249,13 @@ __global__ __launch_bounds__(kThreads, 2) void stage1_mfma_kernel(Stage1Args a, 
       if (q == 0) red[wave][nb * 16 + r] = best;
     }
     __syncthreads();
-    if (tid < BN && b0 + tid < a.B) {
-      uint64_t k = red[0][tid];
+    uint64_t k = 0ull;
+    if (tid < BN) {
+      k = red[0][tid];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) k = umax64(k, red[w][tid]);
-      a.cand[(int64_t)vt * a.B + b0 + tid] = k;
     }
+    publish_candidates(a, vt, b0, min(BN, a.B - b0), k, tid, kThreads);
   }
 }
 
@@ -270,7 +271,9 @@ hipError_t launch_nb(const Stage1Args& a, hipStream_t stream) {
   if (sample && store) k = stage1_mfma_kernel<NB, MB, true, true>;
   else if (sample) k = stage1_mfma_kernel<NB, MB, true, false>;
   else k = stage1_mfma_kernel<NB, MB, false, true>;
-  return launch(k, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, (int32_t)n_bt);
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)G;
+  return launch(k, dim3((unsigned)grid), dim3(kThreads), 0, stream, b, (int32_t)n_bt);
 }
 
 template <int MB>

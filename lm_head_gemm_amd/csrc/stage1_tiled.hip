@@ -214,12 +214,13 @@ __global__ __launch_bounds__(64 * NW) void gemv_tiled_kernel(Stage1Args a) {
     for (int mk = 1; mk < 16; mk <<= 1) best = umax64(best, shfl_xor_u64(best, mk));
     if (r == 0 && q < BB) red[wave][q] = best;
     __syncthreads();
-    if (tid < BB && b0 + tid < a.B) {
-      uint64_t k = red[0][tid];
+    uint64_t k = 0ull;
+    if (tid < BB) {
+      k = red[0][tid];
 #pragma unroll
       for (int w = 1; w < NW; ++w) k = umax64(k, red[w][tid]);
-      a.cand[(int64_t)vt * a.B + b0 + tid] = k;
     }
+    publish_candidates(a, vt, b0, min(BB, a.B - b0), k, tid, 64 * NW);
   }
 }
 
@@ -253,66 +254,68 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   const uint4* wt = static_cast<const uint4*>(a.W) + lane;
   const uint16_t* H = static_cast<const uint16_t*>(a.H);
 
-  auto load_w = [&](int c, uint4 (&w)[kKS]) {
-    const uint4* p = wt + block_piece(mc, c, nC);
+  // This thread's share of each H block: rows hn[i], columns hk[i] .. +8;
+  // pieces past B or D are zero. (Predicated loads measured faster here than
+  // clamped-address loads followed by a select.)
+  int hn[HP], hk[HP];
 #pragma unroll
-    for (int t = 0; t < kKS; ++t) w[t] = has_rows ? load_stream16(p + t * 64) : make_uint4(0u, 0u, 0u, 0u);
-  };
+  for (int i = 0; i < HP; ++i) {
+    const int p = tid + NT * i;
+    hn[i] = p / (kBK / 8);
+    hk[i] = 8 * (p % (kBK / 8));
+  }
   auto load_h = [&](int c, uint4 (&h)[HP]) {
 #pragma unroll
     for (int i = 0; i < HP; ++i) {
-      const int p = tid + NT * i;
-      const int n = p / (kBK / 8);
-      const int k = c * kBK + 8 * (p % (kBK / 8));
+      const int k = c * kBK + hk[i];
       h[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (b0 + n < a.B && k < D) h[i] = *reinterpret_cast<const uint4*>(H + (int64_t)(b0 + n) * a.ldh + k);
+      if (b0 + hn[i] < a.B && k < D) h[i] = *reinterpret_cast<const uint4*>(H + (int64_t)(b0 + hn[i]) * a.ldh + k);
     }
   };
   auto store_h = [&](int buf, const uint4 (&h)[HP]) {
 #pragma unroll
-    for (int i = 0; i < HP; ++i) {
-      const int p = tid + NT * i;
-      *reinterpret_cast<uint4*>(lds_h + buf * BN * kLdsRow + (p / (kBK / 8)) * kLdsRow + 8 * (p % (kBK / 8))) = h[i];
-    }
+    for (int i = 0; i < HP; ++i)
+      *reinterpret_cast<uint4*>(lds_h + buf * BN * kLdsRow + hn[i] * kLdsRow + hk[i]) = h[i];
   };
 
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // W for block c+1 is in flight while block c is multiplied (two register
-  // sets, used alternately); H for block c+1 is loaded during block c and
-  // stored to the other LDS buffer before the workgroup barrier.
-  uint4 w[2][kKS];
+  // Rolling prefetch: the register holding K step t of block c is reloaded
+  // with step t of block c+1 as soon as its MFMAs have been issued, so one
+  // block (8 KiB per wave) stays in flight with a single register set; W
+  // loads are unconditional (clamped row block) so the compiler can count
+  // them. H for block c+1 is loaded during block c and written to the other
+  // LDS buffer before the workgroup barrier.
+  uint4 w[kKS];
   uint4 hreg[HP];
+  {
+    const uint4* p = wt + block_piece(mc, 0, nC);
+#pragma unroll
+    for (int t = 0; t < kKS; ++t) w[t] = load_stream16(p + t * 64);
+  }
   load_h(0, hreg);
   store_h(0, hreg);
-  load_w(0, w[0]);
   __syncthreads();
 
-  for (int c0 = 0; c0 < nC; c0 += 2) {
+  for (int c = 0; c < nC; ++c) {
+    const int cn = min(c + 1, nC - 1);   // the last block reloads itself (unused)
+    load_h(cn, hreg);
+    const uint4* p = wt + block_piece(mc, cn, nC);
+    const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int c = c0 + s;
-      if (c < nC) {
-        const bool more = c + 1 < nC;
-        if (more) {
-          load_h(c + 1, hreg);  // before W: needed first, loads complete in order
-          load_w(c + 1, w[s ^ 1]);
-        }
-        const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow;
+    for (int t = 0; t < kKS; ++t) {
+      const uint4 x = w[t];
+      w[t] = load_stream16(p + t * 64);
 #pragma unroll
-        for (int t = 0; t < kKS; ++t) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
-            acc[nb] = mfma16x16x32(w[s][t], bfrag, acc[nb]);
-          }
-        }
-        if (more) store_h((c + 1) & 1, hreg);
-        __syncthreads();
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
+        acc[nb] = mfma16x16x32(x, bfrag, acc[nb]);
       }
     }
+    store_h((c + 1) & 1, hreg);
+    __syncthreads();
   }
 
   const int v0 = 16 * m + 4 * q;   // this lane's four consecutive vocab rows
@@ -345,12 +348,13 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
       if (q == 0) red[wave][nb * 16 + r] = best;
     }
     __syncthreads();
-    if (tid < BN && b0 + tid < a.B) {
-      uint64_t k = red[0][tid];
+    uint64_t k = 0ull;
+    if (tid < BN) {
+      k = red[0][tid];
 #pragma unroll
       for (int w2 = 1; w2 < NW; ++w2) k = umax64(k, red[w2][tid]);
-      a.cand[(int64_t)vt * a.B + b0 + tid] = k;
     }
+    publish_candidates(a, vt, b0, min(BN, a.B - b0), k, tid, NT);
   }
 }
 
@@ -368,7 +372,9 @@ hipError_t launch_gemv_bb(const Stage1Args& a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  return launch(k, grid, dim3(64 * NW), lds, stream, a);
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)(grid.x * grid.y);
+  return launch(k, grid, dim3(64 * NW), lds, stream, b);
 }
 
 template <int NW>
@@ -391,7 +397,9 @@ hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true>;
   else if (sample) k = mfma_tiled_kernel<NB, NW, true, false>;
   else k = mfma_tiled_kernel<NB, NW, false, true>;
-  return launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, a, (int32_t)n_bt);
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)G;
+  return launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b, (int32_t)n_bt);
 }
 
 template <int NW>

@@ -138,7 +138,17 @@ __global__ __launch_bounds__(kThreads) void probe_read_kernel(const uint4* __res
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(uint64_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    p[i] = 0ull;
+}
+
 }  // namespace
+
+hipError_t launch_fill_zero(uint64_t* p, int64_t n, hipStream_t stream) {
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  return launch(fill_zero_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, stream, p, n);
+}
 
 hipError_t launch_probe_read(const void* src, int64_t bytes, int64_t chunk_bytes, uint32_t* sink,
                              hipStream_t stream) {

@@ -45,7 +45,8 @@ class FsOptions(ctypes.Structure):
         ("stage1_start", ctypes.c_void_p),
         ("stage1_stop", ctypes.c_void_p),
         ("weights_layout", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("single_pass", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -96,6 +97,8 @@ def _load():
     lib.fs_test_philox.argtypes = [c_u64, c_u64, c_i64, c_i64, c_i64, vp, vp]
     lib.fs_test_gumbel.restype = ctypes.c_int
     lib.fs_test_gumbel.argtypes = [vp, c_i64, vp, vp]
+    lib.fs_workspace_reset.restype = ctypes.c_int
+    lib.fs_workspace_reset.argtypes = [vp, c_sz, vp]
     lib.fs_probe_read_blocks.restype = c_i64
     lib.fs_probe_read_blocks.argtypes = [c_i64, c_i64]
     lib.fs_probe_read.restype = ctypes.c_int
@@ -165,8 +168,9 @@ def _check_inputs(H: torch.Tensor, W):
 
 
 def make_options(variant="auto", vocab_tile=0, logits=None, events=None, batch_tile=0,
-                 layout=FS_LAYOUT_ROWS) -> FsOptions:
+                 layout=FS_LAYOUT_ROWS, single_pass=False) -> FsOptions:
     o = FsOptions()
+    o.single_pass = int(bool(single_pass))
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     o.vocab_tile = int(vocab_tile)
     o.batch_tile = int(batch_tile)
@@ -181,13 +185,21 @@ def make_options(variant="auto", vocab_tile=0, logits=None, events=None, batch_t
     return o
 
 
+def workspace_reset(workspace: torch.Tensor, stream=None) -> None:
+    """Zeroes a workspace with the library's fill kernel (fs_workspace_reset)."""
+    _check(_lib.fs_workspace_reset(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "fs_workspace_reset")
+
+
 def num_vocab_tiles(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0, tiled=False) -> int:
     o = make_options(variant, vocab_tile, layout=FS_LAYOUT_TILED if tiled else FS_LAYOUT_ROWS)
     return int(_lib.fs_num_vocab_tiles(B, D, V, _dtype_code(dtype), ctypes.byref(o)))
 
 
-def workspace_bytes(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0, tiled=False) -> int:
-    o = make_options(variant, vocab_tile, layout=FS_LAYOUT_TILED if tiled else FS_LAYOUT_ROWS)
+def workspace_bytes(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0, tiled=False,
+                    single_pass=False) -> int:
+    o = make_options(variant, vocab_tile, layout=FS_LAYOUT_TILED if tiled else FS_LAYOUT_ROWS,
+                     single_pass=single_pass)
     return int(_lib.fs_workspace_bytes_ex(B, D, V, _dtype_code(dtype), ctypes.byref(o)))
 
 
@@ -198,18 +210,21 @@ def unfused_workspace_bytes(B, D, V, dtype=torch.bfloat16, logits_dtype=torch.bf
 def sample_fused(H: torch.Tensor, W, temperature: float, seed: int, step: int,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                  variant="auto", vocab_tile: int = 0, logits: torch.Tensor | None = None,
-                 events=None, stream=None, batch_tile: int = 0) -> torch.Tensor:
+                 events=None, stream=None, batch_tile: int = 0, single_pass: bool = False) -> torch.Tensor:
     """One token per row of H from softmax(H W^T / T) (Gumbel-max, fused).
-    W is a row-major [V, D] tensor or a TiledWeights."""
+    W is a row-major [V, D] tensor or a TiledWeights. With single_pass, a
+    caller-provided workspace must have been zeroed once (workspace_reset)."""
     _check_inputs(H, W)
     B, D = H.shape
     wptr, ldw, V, _, layout = _weights(W)
-    o = make_options(variant, vocab_tile, logits, events, batch_tile, layout)
+    o = make_options(variant, vocab_tile, logits, events, batch_tile, layout, single_pass)
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=H.device)
     if workspace is None:
         nbytes = int(_lib.fs_workspace_bytes_ex(B, D, V, _dtype_code(H.dtype), ctypes.byref(o)))
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=H.device)
+        if single_pass:
+            workspace_reset(workspace, stream)
     st = _lib.fs_sample_fused_ex(H.data_ptr(), H.stride(0), wptr, ldw, _dtype_code(H.dtype), B, D, V,
                                  float(temperature), int(seed), int(step), workspace.data_ptr(),
                                  workspace.numel(), out.data_ptr(), _stream(stream), ctypes.byref(o))

@@ -160,8 +160,16 @@ def test_tiled_layout_validation(lib):
     o.weights_layout = 2
     assert _fused(lib, opts=o) == INVALID
     o = FsOptions()
-    o.reserved = 1
+    o.reserved[1] = 1
     assert _fused(lib, opts=o) == INVALID
+    # single pass: B keys + a counter, independent of the tile count
+    o = FsOptions()
+    o.single_pass = 1
+    assert lib.fs_workspace_bytes_ex(3, 64, 100000, BF16, ctypes.byref(o)) == 512
+    assert _fused(lib, opts=o, wsb=256) == WS_SMALL
+    assert lib.fs_workspace_reset(None, 256, None) == INVALID
+    assert lib.fs_workspace_reset(FAKE, 12, None) == INVALID
+    assert lib.fs_workspace_reset(FAKE + 8, 256, None) == UNSUPPORTED
     o = FsOptions()
     o.weights_layout = 1
     assert _fused(lib, opts=o, dtype=F32) == UNSUPPORTED

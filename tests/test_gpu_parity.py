@@ -179,6 +179,32 @@ def test_tiled_unfused_and_store(fs):
         check_parity(H[rows], W, 1.0, 4, 4, rows, tok)
 
 
+@pytest.mark.parametrize("layout,variant,dtype", [
+    ("rows", "gemv", "bf16"), ("rows", "mfma", "bf16"), ("rows", "gemv", "f32"),
+    ("tiled", "gemv", "bf16"), ("tiled", "mfma", "bf16"),
+])
+@pytest.mark.parametrize("B,D,V", [(1, 256, 4099), (3, 520, 2001), (17, 1032, 3000), (64, 264, 1500),
+                                   (130, 512, 1000)])
+def test_single_pass_equals_two_stage(fs, layout, variant, dtype, B, D, V):
+    """Stage 2 folded into Stage 1 (atomic maximum + last workgroup) gives
+    the two-stage tokens, and leaves its workspace zero for the next call."""
+    import torch
+    if layout == "tiled" and dtype == "f32":
+        pytest.skip("tiled layout is bf16 only")
+    H, W = _rand_head(B * 5 + D + V, B, D, V, dtype)
+    Hd, Wd = to_device(H), to_device(W)
+    Wx = fs.TiledWeights(Wd) if layout == "tiled" else Wd
+    nbytes = fs.workspace_bytes(B, D, V, Hd.dtype, variant=variant, tiled=layout == "tiled", single_pass=True)
+    ws = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda")
+    fs.workspace_reset(ws)
+    for T, seed, step in ((1.0, 0, 0), (0.7, 5, 2**32 + 3), (0.0, 0, 0), (1.0, 9, 1)):
+        two = fs.sample_fused(Hd, Wx, T, seed, step, variant=variant).cpu().numpy()
+        one = fs.sample_fused(Hd, Wx, T, seed, step, variant=variant, single_pass=True, workspace=ws).cpu().numpy()
+        assert np.array_equal(one, two)
+        assert int(ws.count_nonzero()) == 0
+        check_parity(H, W, T, seed, step, np.arange(B), one)
+
+
 def test_batch_prefix_and_repeat_determinism(fs):
     B, D, V = 13, 256, 3001
     H, W = _rand_head(9, B, D, V)
