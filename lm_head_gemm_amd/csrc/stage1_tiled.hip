@@ -299,24 +299,29 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   store_h(0, hreg);
   __syncthreads();
 
-  for (int c = 0; c < nC; ++c) {
-    const int cn = min(c + 1, nC - 1);   // the last block reloads itself (unused)
-    load_h(cn, hreg);
-    const uint4* p = wt + block_piece(mc, cn, nC);
+  // Block c's math; with `more`, block c+1's loads are issued on the way.
+  // The last block is peeled off so no load is ever issued for nothing.
+  auto step = [&](int c, bool more) {
+    if (more) load_h(c + 1, hreg);
+    const uint4* p = wt + block_piece(mc, more ? c + 1 : c, nC);
     const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow;
 #pragma unroll
     for (int t = 0; t < kKS; ++t) {
       const uint4 x = w[t];
-      w[t] = load_stream16(p + t * 64);
+      if (more) w[t] = load_stream16(p + t * 64);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
         acc[nb] = mfma16x16x32(x, bfrag, acc[nb]);
       }
     }
-    store_h((c + 1) & 1, hreg);
-    __syncthreads();
-  }
+    if (more) {
+      store_h((c + 1) & 1, hreg);
+      __syncthreads();
+    }
+  };
+  for (int c = 0; c + 1 < nC; ++c) step(c, true);
+  step(nC - 1, false);
 
   const int v0 = 16 * m + 4 * q;   // this lane's four consecutive vocab rows
   if constexpr (STORE) {

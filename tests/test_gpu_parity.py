@@ -329,26 +329,46 @@ def full_workload(request):
 
 
 def test_full_size_sampled_rows(fs, full_workload):
-    """Every B of the workload's sweep, in the default launch configuration.
-    H for a smaller B is a prefix of H, and a row's noise is keyed by its
-    index, so one oracle pass over the union of sampled rows serves all B."""
+    """Every B of the workload's sweep, in the launch configurations the
+    benchmark times: row-major W and the tiled layout, two-stage and
+    single-pass. H for a smaller B is a prefix of H, and a row's noise is
+    keyed by its index, so one oracle pass over the union of sampled rows
+    serves all B."""
+    import torch
     wl, H, W = full_workload
     Hd, Wd = to_device(H), to_device(W)
+    tw = fs.TiledWeights(Wd)
     rng = np.random.default_rng(wl.seed)
     picked = {}
     for B in wl.batches:
-        tok = fs.sample_fused(Hd[:B], Wd, wl.temperature, wl.seed, 0).cpu().numpy()
-        assert tok.min() >= 0 and tok.max() < wl.V
         rows = np.unique(np.concatenate([[0, B - 1], rng.choice(B, size=min(B, 6), replace=False)]))
-        picked[B] = (rows, tok[rows])
-    union = np.unique(np.concatenate([r for r, _ in picked.values()]))
+        toks = {}
+        toks["rows"] = fs.sample_fused(Hd[:B], Wd, wl.temperature, wl.seed, 0).cpu().numpy()
+        toks["tiled"] = fs.sample_fused(Hd[:B], tw, wl.temperature, wl.seed, 0).cpu().numpy()
+        toks["tiled-single"] = fs.sample_fused(Hd[:B], tw, wl.temperature, wl.seed, 0,
+                                               single_pass=True).cpu().numpy()
+        if B <= 16:
+            # a vocab tile that does not divide V: the last tile is ragged
+            ragged = fs.sample_fused(Hd[:B], Wd, wl.temperature, wl.seed, 0, variant="gemv",
+                                     vocab_tile=1008).cpu().numpy()
+            assert wl.V % 1008 != 0
+            assert np.array_equal(ragged, toks["rows"])
+        for name, tok in toks.items():
+            assert tok.min() >= 0 and tok.max() < wl.V, name
+        # every launch configuration agrees on every row (not only the sampled ones)
+        assert np.array_equal(toks["tiled"], toks["tiled-single"])
+        same = toks["rows"] == toks["tiled"]
+        picked[B] = (rows, toks, np.flatnonzero(~same))
+    union = np.unique(np.concatenate([np.concatenate([r, d]) for r, _, d in picked.values()]))
     ref = oracle.sample(H, W, wl.temperature, wl.seed, 0, rows=union)
     pos = {int(r): k for k, r in enumerate(union)}
     total = near = 0
-    for B, (rows, tok) in picked.items():
-        sel = [pos[int(r)] for r in rows]
+    for B, (rows, toks, diff) in picked.items():
+        check_rows = np.unique(np.concatenate([rows, diff]))
+        sel = [pos[int(r)] for r in check_rows]
         sub = oracle.SampleResult(ref.idx[sel], ref.best[sel], ref.second[sel], ref.second_idx[sel])
-        n, k = check_parity(H, W, wl.temperature, wl.seed, 0, rows, tok, ref=sub)
-        total += n
-        near += k
+        for name in ("rows", "tiled"):
+            n, k = check_parity(H, W, wl.temperature, wl.seed, 0, check_rows, toks[name][check_rows], ref=sub)
+            total += n
+            near += k
     print(f"{wl.name}: {total} row checks over B={list(wl.batches)}, near-tie fraction {near / total:.4f}")
