@@ -74,15 +74,19 @@ typedef enum fs_layout { FS_LAYOUT_ROWS = 0, FS_LAYOUT_TILED = 1 } fs_layout_t;
 typedef struct fs_options {
   int32_t variant;         /* fs_variant_t */
   int32_t vocab_tile;      /* rows per Stage-1 vocab tile; 0 = variant default.
-                              Must be a multiple of the variant's granule
-                              (fs_vocab_tile_granule). */
+                              Row-major W: a multiple of the variant's granule
+                              (fs_vocab_tile_granule). Tiled W: 64 or 128, or
+                              256 for MFMA (the wide kernel: 8 waves of two
+                              16-row blocks, 128-column batch tiles; the
+                              default from B = 65 on). */
   void* logits;            /* non-null: the fused call also stores l = H W^T
                               (device [B, V] row-major, stride ld_logits) */
   int64_t ld_logits;
   int32_t logits_dtype;    /* fs_dtype_t of the stored logits */
   int32_t batch_tile;      /* MFMA only: batch rows per workgroup (16, 32 or
-                              64); 0 = chosen from B. Larger batches are split
-                              into tiles that re-read W from L2. */
+                              64; 128 with the 256-row tiled tile, and only
+                              there); 0 = chosen from B. Larger batches are
+                              split into tiles that re-read W from L2. */
   hipEvent_t stage1_start; /* non-null: recorded on `stream` right before and */
   hipEvent_t stage1_stop;  /* right after the Stage-1 launch (for timing) */
   int32_t weights_layout;  /* fs_layout_t of W */

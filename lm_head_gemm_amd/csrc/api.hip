@@ -19,6 +19,9 @@ constexpr int32_t kGemvDefaultTile = 16;
 constexpr int32_t kMfmaGranule = 64;
 constexpr int32_t kTiledGemvTile = 128;    // tiled layout: 8 waves x 16 rows
 constexpr int32_t kTiledMfmaTile = 128;     // tiled layout: 8 waves x 16 rows
+constexpr int32_t kTiledWideTile = 256;     // tiled layout: 8 waves x 2 x 16 rows
+constexpr int32_t kTiledWideBatch = 128;    // batch tile of the wide kernel
+constexpr int64_t kTiledWideMinB = 65;      // batches from here on use the wide kernel
 constexpr int32_t kMfmaSmallBTile = 64;    // one 16-row block per wave
 constexpr int32_t kMfmaLargeBTile = 128;    // two blocks per wave above 32 rows
 constexpr int64_t kGemvMaxB = 2;            // bf16 batches above this use the MFMA kernel
@@ -53,7 +56,8 @@ struct Plan {
 //   Row-major W: GEMV for fp32 inputs and bf16 batches up to kGemvMaxB rows
 //     (vocab tile: multiple of 16 rows), MFMA above (64 or 128 rows).
 //   Tiled W (bf16): the same split; vocab tile 64 or 128 rows (4 or 8 waves
-//     of one 16-row block each).
+//     of one 16-row block each), and for MFMA batches from 65 rows on the
+//     256-row wide tile (8 waves of two blocks, batch tile 128).
 bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* o, Plan* p,
                fs_status_t* why) {
   (void)D;
@@ -67,14 +71,17 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
     variant = (dtype == FS_DTYPE_BF16 && B > kGemvMaxB) ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
   int32_t tile = o ? o->vocab_tile : 0;
   const int32_t bt = o ? o->batch_tile : 0;
-  if (bt != 0 && bt != 16 && bt != 32 && bt != 64) return false;
+  if (bt != 0 && bt != 16 && bt != 32 && bt != 64 && bt != kTiledWideBatch) return false;
   if (layout == FS_LAYOUT_TILED) {
     if (dtype != FS_DTYPE_BF16) {
       *why = FS_ERR_UNSUPPORTED;
       return false;
     }
-    if (tile == 0) tile = variant == FS_VARIANT_MFMA ? kTiledMfmaTile : kTiledGemvTile;
-    if (tile != 64 && tile != 128) return false;
+    if (tile == 0)
+      tile = variant != FS_VARIANT_MFMA ? kTiledGemvTile : B >= kTiledWideMinB ? kTiledWideTile : kTiledMfmaTile;
+    const bool wide = variant == FS_VARIANT_MFMA && tile == kTiledWideTile;
+    if (tile != 64 && tile != 128 && !wide) return false;
+    if (wide != (bt == kTiledWideBatch) && bt != 0) return false;  // 128-column batch tiles only with the wide tile
   } else if (variant == FS_VARIANT_MFMA) {
     if (dtype != FS_DTYPE_BF16) {
       *why = FS_ERR_UNSUPPORTED;

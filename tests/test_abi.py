@@ -181,6 +181,23 @@ def test_tiled_layout_validation(lib):
     # ldw is ignored for the tiled layout; the other checks still apply
     o.batch_tile = 0
     assert _fused(lib, opts=o, ldw=0, wsb=8) == WS_SMALL
+    # the 256-row wide tile: MFMA only, default from B = 65 on, batch tile 128 only there
+    o = FsOptions()
+    o.weights_layout = 1
+    assert lib.fs_num_vocab_tiles(64, 4096, 128256, BF16, ctypes.byref(o)) == 1002
+    assert lib.fs_num_vocab_tiles(65, 4096, 128256, BF16, ctypes.byref(o)) == 501
+    o.vocab_tile = 256
+    assert lib.fs_num_vocab_tiles(8, 4096, 1000, BF16, ctypes.byref(o)) == 4
+    o.batch_tile = 64
+    assert lib.fs_num_vocab_tiles(8, 4096, 1000, BF16, ctypes.byref(o)) == -1
+    o.batch_tile = 128
+    assert lib.fs_num_vocab_tiles(8, 4096, 1000, BF16, ctypes.byref(o)) == 4
+    o.vocab_tile = 128
+    assert lib.fs_num_vocab_tiles(8, 4096, 1000, BF16, ctypes.byref(o)) == -1
+    o.vocab_tile = 256
+    o.batch_tile = 0
+    o.variant = 1  # GEMV
+    assert lib.fs_num_vocab_tiles(8, 4096, 1000, BF16, ctypes.byref(o)) == -1
     base = [FAKE, 64, FAKE, 64, BF16, 2, 64, 1000, 1.0, 0, 0, F32, FAKE, 1 << 20, FAKE, None]
     o = FsOptions()
     o.weights_layout = 3

@@ -147,10 +147,11 @@ def test_pack_weights_tiled_layout(fs, V, D):
     assert got.shape == want.shape and np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("variant,tile", [("auto", 0), ("gemv", 64), ("gemv", 128), ("mfma", 64), ("mfma", 128)])
+@pytest.mark.parametrize("variant,tile", [("auto", 0), ("gemv", 64), ("gemv", 128), ("mfma", 64), ("mfma", 128),
+                                          ("mfma", 256)])
 @pytest.mark.parametrize("B,D,V", [
     (1, 64, 5), (2, 520, 2001), (3, 256, 777), (4, 1032, 3000), (16, 256, 4099),
-    (33, 4096, 2053), (64, 264, 1500), (100, 512, 1000),
+    (33, 4096, 2053), (64, 264, 1500), (100, 512, 1000), (129, 1032, 3001), (260, 264, 4099),
 ])
 def test_tiled_layout_parity(fs, variant, tile, B, D, V):
     H, W = _rand_head(B * 11 + D + V, B, D, V)
@@ -177,6 +178,33 @@ def test_tiled_unfused_and_store(fs):
                                 variant=var).cpu().numpy()
         rows = np.arange(3 if var == "gemv" else B)
         check_parity(H[rows], W, 1.0, 4, 4, rows, tok)
+
+
+def test_tiled_wide_store_and_unfused(fs):
+    """The 256-row wide kernel (batches above 64) in its store and store-only
+    forms: logits exact to fp32 rounding, ragged V and D, two batch tiles."""
+    import torch
+    B, D, V = 150, 1032, 2001
+    H, W = _rand_head(23, B, D, V)
+    Hd = to_device(H)
+    tw = fs.TiledWeights(to_device(W))
+    assert fs.num_vocab_tiles(B, D, V, tiled=True) == (V + 255) // 256
+    exact = oracle.exact_logits(H, W)
+    l32 = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda")
+    tok = fs.sample_fused(Hd, tw, 1.0, 4, 4, logits=l32).cpu().numpy()
+    assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - exact)) < 1e-4
+    check_parity(H, W, 1.0, 4, 4, np.arange(B), tok)
+    l16 = torch.zeros((B, V + 5), dtype=torch.bfloat16, device="cuda")
+    fs.sample_fused(Hd, tw, 1.0, 4, 4, logits=l16[:, :V])
+    got16 = l16[:, :V].float().cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got16 - exact) / np.maximum(np.abs(exact), 1e-3)) < 2 ** -8
+    assert int(l16[:, V:].count_nonzero()) == 0
+    for ld in (torch.float32, torch.bfloat16):
+        tok = fs.sample_unfused(Hd, tw, 0.8, 6, 1, logits_dtype=ld).cpu().numpy()
+        if ld == torch.float32:
+            check_parity(H, W, 0.8, 6, 1, np.arange(B), tok)
+        else:
+            assert tok.min() >= 0 and tok.max() < V
 
 
 @pytest.mark.parametrize("layout,variant,dtype", [
