@@ -36,7 +36,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKS = 8;               // MFMA K steps (of 32) per K chunk
 constexpr int kBK = 32 * kKS;        // 256
-constexpr int kLdsRow = kBK + 8;     // padded H row in LDS (elements)
+constexpr int kLdsRow = kBK + 16;    // padded H row in LDS (elements): a stride of an odd multiple of 32 bytes reads conflict-free
 constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

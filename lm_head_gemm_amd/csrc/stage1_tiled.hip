@@ -37,7 +37,11 @@ namespace {
 constexpr int kBK = 256;            // columns per block
 constexpr int kKS = 8;              // K steps of 32 per block
 constexpr int kBlock16 = kKS * 64;  // 16-byte pieces per block
-constexpr int kLdsRow = kBK + 8;    // padded H row in LDS (elements)
+// Padded H row in LDS (elements). The 32-byte pad makes the row stride an odd
+// multiple of 32 bytes, which measured free of bank conflicts for the B
+// operand reads (16 lanes of 16 rows per access); a 16-byte pad conflicts
+// 2-way on gfx950.
+constexpr int kLdsRow = kBK + 16;
 constexpr int kXcds = 8;
 constexpr int kGroup = 8;           // row blocks per group in the tiled layout
 
@@ -392,7 +396,7 @@ constexpr int kWideRows = 16 * kWideNW * kWideMB;
 template <bool SAMPLE, bool STORE>
 __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int NB = kWideNB, NW = kWideNW, MB = kWideMB, KSUB = kWideKSub, PD = kWidePD;
-  constexpr int BN = kWideBN, NT = 64 * NW, KH = 32 * KSUB, ROW = KH + 8;
+  constexpr int BN = kWideBN, NT = 64 * NW, KH = 32 * KSUB, ROW = KH + 16;   // 160-byte rows: conflict-free reads
   constexpr int HP = BN * (KH / 8) / NT;       // 16-byte pieces of H per thread per sub-chunk
   constexpr int NSUB = kKS / KSUB;
   static_assert(HP >= 1 && HP * NT == BN * (KH / 8), "batch tile vs workgroup size");
