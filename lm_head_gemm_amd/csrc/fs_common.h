@@ -95,6 +95,28 @@ __device__ __forceinline__ uint64_t pack_key(float s, uint32_t v) {
   return (s != s) ? 0ull : key;
 }
 
+// Running argmax of one lane over candidates presented in increasing vocab
+// order: a strictly greater score replaces the best, so equal scores keep the
+// lowest index; a NaN best (the initial state) is replaced by anything, and a
+// NaN candidate never replaces a number. Its key equals the maximum of the
+// candidates' pack_key values (0 when there were none or all were NaN).
+struct RunMax {
+  float s;
+  int32_t v;
+};
+
+__device__ __forceinline__ RunMax runmax_init() { return RunMax{__builtin_nanf(""), -1}; }
+
+__device__ __forceinline__ void runmax_take(RunMax& m, float s, int32_t v) {
+  const bool take = s > m.s || m.s != m.s;
+  m.s = take ? s : m.s;
+  m.v = take ? v : m.v;
+}
+
+__device__ __forceinline__ uint64_t runmax_key(const RunMax& m) {
+  return m.v < 0 ? 0ull : pack_key(m.s, (uint32_t)m.v);
+}
+
 __device__ __forceinline__ int32_t key_to_token(uint64_t key) {
   return key == 0ull ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)key);
 }

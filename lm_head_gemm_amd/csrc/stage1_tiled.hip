@@ -29,6 +29,8 @@
 //    H staged in sub-chunks and the B operands read one K step ahead.
 // All end in the same register epilogue: l * (1/T) + Gumbel(Philox word),
 // packed-key maximum per batch row, one candidate per (row, vocab tile).
+#include <type_traits>
+
 #include "fs_common.h"
 
 namespace fs {
@@ -342,22 +344,37 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
     }
   }
   if constexpr (SAMPLE) {
+    // As in the wide kernel: running maximum over the lane's four rows in
+    // vocab order, bound check on v only in the last vocab tile, no noise
+    // when greedy; columns past B are dropped by publish_candidates.
+    auto tile_max = [&](auto greedy_c, auto full_c) {
+      constexpr bool kGreedy = decltype(greedy_c)::value;
+      constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int b = b0 + nb * 16 + r;
-      uint4 words = make_uint4(0u, 0u, 0u, 0u);
-      if (!a.greedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
-      uint64_t best = 0ull;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int b = b0 + nb * 16 + r;
+        uint4 words = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (!kGreedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
+        RunMax best = runmax_init();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float l = acc[nb][j];
-        const float s = a.greedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, j)));
-        const bool valid = has_rows && v0 + j < a.V && b < a.B;
-        best = umax64(best, valid ? pack_key(s, (uint32_t)(v0 + j)) : 0ull);
+        for (int j = 0; j < 4; ++j) {
+          const float l = acc[nb][j];
+          const float s = kGreedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, j)));
+          if (kFull || v0 + j < a.V) runmax_take(best, s, v0 + j);
+        }
+        uint64_t key = runmax_key(best);
+        key = umax64(key, shfl_xor_u64(key, 16));
+        key = umax64(key, shfl_xor_u64(key, 32));
+        if (q == 0) red[wave][nb * 16 + r] = key;
       }
-      best = umax64(best, shfl_xor_u64(best, 16));
-      best = umax64(best, shfl_xor_u64(best, 32));
-      if (q == 0) red[wave][nb * 16 + r] = best;
+    };
+    const bool full = (int64_t)(vt + 1) * NW * 16 <= a.V;
+    if (a.greedy) {
+      if (full) tile_max(std::true_type{}, std::true_type{});
+      else tile_max(std::true_type{}, std::false_type{});
+    } else {
+      if (full) tile_max(std::false_type{}, std::true_type{});
+      else tile_max(std::false_type{}, std::false_type{});
     }
     __syncthreads();
     uint64_t k = 0ull;
@@ -532,26 +549,43 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
     }
   }
   if constexpr (SAMPLE) {
+    // Per batch column: the lane's 4 x MB candidates come in increasing
+    // vocab order (a running maximum suffices), then the four lanes of the
+    // column combine their keys. Batch columns past B are computed on zero
+    // rows and dropped by publish_candidates. Only the last vocab tile needs
+    // the bound check on v; greedy (T = 0) skips the noise entirely.
+    auto tile_max = [&](auto greedy_c, auto full_c) {
+      constexpr bool kGreedy = decltype(greedy_c)::value;
+      constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int b = b0 + nb * 16 + r;
-      uint64_t best = 0ull;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int b = b0 + nb * 16 + r;
+        RunMax best = runmax_init();
 #pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        const int v0 = 16 * m[j] + 4 * q;   // this lane's four consecutive vocab rows
-        uint4 words = make_uint4(0u, 0u, 0u, 0u);
-        if (!a.greedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
+        for (int j = 0; j < MB; ++j) {
+          const int v0 = 16 * m[j] + 4 * q;   // this lane's four consecutive vocab rows
+          uint4 words = make_uint4(0u, 0u, 0u, 0u);
+          if constexpr (!kGreedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float l = acc[j][nb][e];
-          const float sc = a.greedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, e)));
-          const bool valid = m[j] < nM && v0 + e < a.V && b < a.B;
-          best = umax64(best, valid ? pack_key(sc, (uint32_t)(v0 + e)) : 0ull);
+          for (int e = 0; e < 4; ++e) {
+            const float l = acc[j][nb][e];
+            const float sc = kGreedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, e)));
+            if (kFull || v0 + e < a.V) runmax_take(best, sc, v0 + e);
+          }
         }
+        uint64_t key = runmax_key(best);
+        key = umax64(key, shfl_xor_u64(key, 16));
+        key = umax64(key, shfl_xor_u64(key, 32));
+        if (q == 0) red[wave][nb * 16 + r] = key;
       }
-      best = umax64(best, shfl_xor_u64(best, 16));
-      best = umax64(best, shfl_xor_u64(best, 32));
-      if (q == 0) red[wave][nb * 16 + r] = best;
+    };
+    const bool full = (int64_t)(vt + 1) * kWideRows <= a.V;
+    if (a.greedy) {
+      if (full) tile_max(std::true_type{}, std::true_type{});
+      else tile_max(std::true_type{}, std::false_type{});
+    } else {
+      if (full) tile_max(std::false_type{}, std::true_type{});
+      else tile_max(std::false_type{}, std::false_type{});
     }
     __syncthreads();
     uint64_t k = 0ull;
