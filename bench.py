@@ -33,12 +33,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The sources the timed Stage-1 kernel (tiled layout) and its launch are built
+# from: a traffic record is valid only while they are unchanged.
+STAGE1_SOURCES = ("include/flashsample.h", "lm_head_gemm_amd/csrc/fs_common.h",
+                  "lm_head_gemm_amd/csrc/stage1_tiled.hip", "lm_head_gemm_amd/csrc/api.hip")
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources: identifies the kernels a traffic record belongs to."""
+    """Hash of STAGE1_SOURCES: identifies the kernel a traffic record belongs to."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "lm_head_gemm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
+    for f in STAGE1_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -110,6 +115,28 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
     torch.cuda.synchronize()
     s1 = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     return total_ms / steps, s1, n_warm
+
+
+def time_fused_store(fs, Hb, Ws, wl, steps, warmup, B, min_warm_ms=0.0):
+    """ms per step of the fused call with its store-logits option (bf16
+    logits written beside the sample), timed like time_fused."""
+    import torch
+    T, seed = wl.temperature, wl.seed
+    tiled = isinstance(Ws[0], fs.TiledWeights)
+    ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, tiled=tiled), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, wl.V), dtype=torch.bfloat16, device="cuda")
+    kw = dict(out=out, workspace=ws, logits=logits)
+    warm(lambda i: fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw), warmup, min_warm_ms)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
 
 def time_unfused(fs, Hb, Ws, wl, steps, warmup, B, logits_dtype, min_warm_ms=0.0):
@@ -198,7 +225,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the whole vocabulary "
-              f"fits one MI355X, and this build has no multi-GPU path)", file=sys.stderr)
+              f"fits one MI355X; the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -246,17 +273,32 @@ def main():
         tiled = isinstance(weights[0], fs.TiledWeights)
         nt = fs.num_vocab_tiles(b, wl.D, wl.V, Hb.dtype, args.variant, args.vocab_tile, tiled=tiled)
         byts = stage1_bytes(b, wl.D, wl.V, esz, nt)
+        flops = 2 * b * wl.V * wl.D
         rec = {"B": b, "ms_per_step": ms, "samples_per_s": b / (ms * 1e-3), "stage1_ms": s1,
                "stage1_GBps": byts / (s1 * 1e-3) / 1e9, "stage1_bytes": byts, "n_tiles": nt,
-               "flops": 2 * b * wl.V * wl.D, "warmup_steps_run": n_warm}
+               "hbm_frac": byts / (s1 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               "flops": flops, "stage1_TFLOPs": flops / (s1 * 1e-3) / 1e12,
+               "mfma_frac": flops / (s1 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+               "warmup_steps_run": n_warm}
         if not args.no_unfused:
             u16 = time_unfused(fs, Hb, weights, wl, args.steps, args.warmup, b, torch.bfloat16,
                                args.min_warmup_ms)
             rec["unfused_bf16_ms_per_step"] = u16
             rec["fused_speedup_vs_unfused_bf16"] = u16 / ms
+            # IO model (Section 3): with bf16 logits, the unfused path moves
+            # 2*B*V*2 bytes more than the fused one (write + read back) and the
+            # store-logits option B*V*2 more (write), on top of the V*D*2 of W.
+            st = time_fused_store(fs, Hb, weights, wl, args.steps, args.warmup, b, args.min_warmup_ms)
+            rec["io_model"] = {"store_logits_ms_per_step": st,
+                               "store_overhead": st / ms - 1.0,
+                               "store_overhead_predicted": b / wl.D,
+                               "unfused_overhead": u16 / ms - 1.0,
+                               "unfused_overhead_predicted": 2 * b / wl.D}
         log(f"[bench] B={b}: {ms * 1e3:.1f} us/step, stage1 {s1 * 1e3:.1f} us "
-            f"({rec['stage1_GBps']:.0f} GB/s)" +
-            (f", unfused {rec['unfused_bf16_ms_per_step'] * 1e3:.1f} us" if not args.no_unfused else ""))
+            f"({rec['stage1_GBps']:.0f} GB/s, {rec['stage1_TFLOPs']:.0f} TFLOP/s)" +
+            (f", unfused {rec['unfused_bf16_ms_per_step'] * 1e3:.1f} us, store-logits overhead "
+             f"{rec['io_model']['store_overhead'] * 100:+.1f}% (IO model {b / wl.D * 100:+.1f}%)"
+             if not args.no_unfused else ""))
         return rec
 
     Ws_rows = Ws
@@ -328,6 +370,7 @@ def main():
         result["unfused_bf16"] = {"ms_per_step": head["unfused_bf16_ms_per_step"],
                                   "samples_per_s": B / (head["unfused_bf16_ms_per_step"] * 1e-3),
                                   "fused_speedup": head["fused_speedup_vs_unfused_bf16"]}
+        result["io_model"] = head["io_model"]
     if sweep:
         result["sweep"] = [head] + sweep
     if not args.no_cpu_baseline:

@@ -175,28 +175,9 @@ __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
       const float l3 = __shfl_xor(l, 3 << S);
       const bool writer = (lane & ((4 << S) - 1)) == 0 && my_batch < a.B;
       if (writer) {
-        const int64_t off = (int64_t)my_batch * a.ld_logits + row0;
-        if (a.logits_bf16) {
-          uint16_t* p = static_cast<uint16_t*>(a.logits) + off;
-          const uint16_t q[4] = {f32_to_bf16_rne(l), f32_to_bf16_rne(l1), f32_to_bf16_rne(l2),
-                                 f32_to_bf16_rne(l3)};
-          if (row0 + 3 < wave_end && (off & 3) == 0) {
-            *reinterpret_cast<uint2*>(p) =
-                make_uint2((uint32_t)q[0] | ((uint32_t)q[1] << 16), (uint32_t)q[2] | ((uint32_t)q[3] << 16));
-          } else {
-            for (int r = 0; r < kRows; ++r)
-              if (row0 + r < wave_end) p[r] = q[r];
-          }
-        } else {
-          float* p = static_cast<float*>(a.logits) + off;
-          if (row0 + 3 < wave_end && (off & 3) == 0) {
-            *reinterpret_cast<float4*>(p) = make_float4(l, l1, l2, l3);
-          } else {
-            const float q[4] = {l, l1, l2, l3};
-            for (int r = 0; r < kRows; ++r)
-              if (row0 + r < wave_end) p[r] = q[r];
-          }
-        }
+        static_assert(kRows == 4, "one row group = four consecutive vocab rows");
+        const float q[4] = {l, l1, l2, l3};
+        store_logits4(a, my_batch, row0, wave_end, q);
       }
     }
 

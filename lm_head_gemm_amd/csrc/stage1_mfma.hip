@@ -201,27 +201,8 @@ __global__ __launch_bounds__(kThreads, 2) void stage1_mfma_kernel(Stage1Args a, 
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int v0 = row0 + 16 * mb + 4 * q;
-        const f32x4 l = acc[mb][nb];
-        const int64_t off = (int64_t)b * a.ld_logits + v0;
-        if (a.logits_bf16) {
-          uint16_t* p = static_cast<uint16_t*>(a.logits) + off;
-          if (v0 + 3 < tile_end && (off & 3) == 0) {
-            *reinterpret_cast<uint2*>(p) =
-                make_uint2((uint32_t)f32_to_bf16_rne(l[0]) | ((uint32_t)f32_to_bf16_rne(l[1]) << 16),
-                           (uint32_t)f32_to_bf16_rne(l[2]) | ((uint32_t)f32_to_bf16_rne(l[3]) << 16));
-          } else {
-            for (int j = 0; j < 4; ++j)
-              if (v0 + j < tile_end) p[j] = f32_to_bf16_rne(l[j]);
-          }
-        } else {
-          float* p = static_cast<float*>(a.logits) + off;
-          if (v0 + 3 < tile_end && (off & 3) == 0) {
-            *reinterpret_cast<float4*>(p) = make_float4(l[0], l[1], l[2], l[3]);
-          } else {
-            for (int j = 0; j < 4; ++j)
-              if (v0 + j < tile_end) p[j] = l[j];
-          }
-        }
+        const float l[4] = {acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]};
+        store_logits4(a, b, v0, tile_end, l);
       }
     }
   }

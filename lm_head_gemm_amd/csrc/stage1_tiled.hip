@@ -86,28 +86,6 @@ __device__ __forceinline__ bool tile_of(int L, int n_vt, int n_bt, int* vt, int*
   return true;
 }
 
-__device__ __forceinline__ void store_logits4(const Stage1Args& a, int b, int v0, int v_end, const float (&l)[4]) {
-  const int64_t off = (int64_t)b * a.ld_logits + v0;
-  if (a.logits_bf16) {
-    uint16_t* p = static_cast<uint16_t*>(a.logits) + off;
-    if (v0 + 3 < v_end && (off & 3) == 0) {
-      *reinterpret_cast<uint2*>(p) =
-          make_uint2((uint32_t)f32_to_bf16_rne(l[0]) | ((uint32_t)f32_to_bf16_rne(l[1]) << 16),
-                     (uint32_t)f32_to_bf16_rne(l[2]) | ((uint32_t)f32_to_bf16_rne(l[3]) << 16));
-    } else {
-      for (int j = 0; j < 4; ++j)
-        if (v0 + j < v_end) p[j] = f32_to_bf16_rne(l[j]);
-    }
-  } else {
-    float* p = static_cast<float*>(a.logits) + off;
-    if (v0 + 3 < v_end && (off & 3) == 0) {
-      *reinterpret_cast<float4*>(p) = make_float4(l[0], l[1], l[2], l[3]);
-    } else {
-      for (int j = 0; j < 4; ++j)
-        if (v0 + j < v_end) p[j] = l[j];
-    }
-  }
-}
 
 // ---------------------------------------------------------------- pack
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W, int64_t ldw, int32_t V,
@@ -233,6 +211,38 @@ __global__ __launch_bounds__(64 * NW) void gemv_tiled_kernel(Stage1Args a) {
   }
 }
 
+// Logits store of the MFMA kernels, staged through LDS. In the accumulator
+// layout lane (r, q) of wave w holds, per 16-column batch block, the logits of
+// vocab rows v_base + 16w + 4q .. +3 for one batch column, so a direct store
+// writes 8- or 16-byte pieces of 16 different logits rows per instruction.
+// Here each pass moves NBC column blocks: the fragments go to a [16 NBC][16 NW]
+// fp32 tile in LDS (row pitch 16 NW + 8 floats, an odd multiple of 32 bytes),
+// then the workgroup writes whole row segments of 16 NW logits. The caller
+// must have synchronised the workgroup before the first pass (T reuses the H
+// buffers). Rows past B and vocab entries past V are not written.
+template <int NW, int NBC>
+__device__ __forceinline__ void store_logits_staged(const Stage1Args& a, float* T, int v_base, int b_base,
+                                                    const f32x4 (&vals)[NBC], int tid) {
+  constexpr int VW = 16 * NW;          // vocab rows of the tile
+  constexpr int PITCH = VW + 8;
+  constexpr int PER_ROW = VW / 4;      // float4 per staged row
+  const int lane = tid & 63, wave = tid >> 6, r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NBC; ++i)
+    *reinterpret_cast<f32x4*>(T + (16 * i + r) * PITCH + 16 * wave + 4 * q) = vals[i];
+  __syncthreads();
+  for (int p = tid; p < 16 * NBC * PER_ROW; p += 64 * NW) {
+    const int row = p / PER_ROW, c4 = p - row * PER_ROW;
+    const int b = b_base + row;
+    if (b < a.B) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(T + row * PITCH + 4 * c4);
+      const float l[4] = {x[0], x[1], x[2], x[3]};
+      store_logits4(a, b, v_base + 4 * c4, a.V, l);
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- MFMA
 template <int NB, int NW, bool SAMPLE, bool STORE>
 __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
@@ -258,7 +268,6 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   const int nC = (D + kBK - 1) / kBK;
   const int nM = (a.V + 15) / 16;
   const int m = vt * NW + wave;
-  const bool has_rows = m < nM;
   const int mc = min(m, nM - 1);
   const uint4* wt = static_cast<const uint4*>(a.W) + lane;
   const uint16_t* H = static_cast<const uint16_t*>(a.H);
@@ -334,13 +343,16 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
 
   const int v0 = 16 * m + 4 * q;   // this lane's four consecutive vocab rows
   if constexpr (STORE) {
+    constexpr int NBC = NB < 2 ? NB : 2;   // 16-column blocks per staging pass
+    static_assert(16 * NBC * (16 * NW + 8) * 4 <= (int)sizeof(lds_h4), "staging tile fits the H buffers");
+    __syncthreads();                        // every wave is done reading H
+    float* T = reinterpret_cast<float*>(lds_h4);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int b = b0 + nb * 16 + r;
-      if (b < a.B && has_rows) {
-        const float l[4] = {acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]};
-        store_logits4(a, b, v0, a.V, l);
-      }
+    for (int p = 0; p < NB / NBC; ++p) {
+      f32x4 vals[NBC];
+#pragma unroll
+      for (int i = 0; i < NBC; ++i) vals[i] = acc[p * NBC + i];
+      store_logits_staged<NW, NBC>(a, T, vt * NW * 16, b0 + p * NBC * 16, vals, tid);
     }
   }
   if constexpr (SAMPLE) {
@@ -535,16 +547,18 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
   step(nC - 1, true);
 
   if constexpr (STORE) {
+    constexpr int NBC = 2;                  // 16-column blocks per staging pass
+    static_assert(16 * NBC * (16 * NW + 8) * 4 <= (int)sizeof(lds_h4), "staging tile fits the H buffers");
+    __syncthreads();                        // every wave is done reading H
+    float* T = reinterpret_cast<float*>(lds_h4);
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
-      const int v0 = 16 * m[j] + 4 * q;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int b = b0 + nb * 16 + r;
-        if (b < a.B && m[j] < nM) {
-          const float l[4] = {acc[j][nb][0], acc[j][nb][1], acc[j][nb][2], acc[j][nb][3]};
-          store_logits4(a, b, v0, a.V, l);
-        }
+      for (int p = 0; p < NB / NBC; ++p) {
+        f32x4 vals[NBC];
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) vals[i] = acc[j][p * NBC + i];
+        store_logits_staged<NW, NBC>(a, T, 16 * (vt * NW * MB + j * NW), b0 + p * NBC * 16, vals, tid);
       }
     }
   }
