@@ -9,7 +9,7 @@ kernel's achieved HBM bandwidth against MI355X's 8 TB/s, the unfused
 baseline and the row-major layout beside it, and the CPU oracle's rate.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--batch B] [--sweep]
-                  [--layout tiled|rows] [--probe]
+                  [--layout auto|tiled|rows] [--probe]
 """
 from __future__ import annotations
 
@@ -210,8 +210,9 @@ def main():
     ap.add_argument("--batch-tile", type=int, default=0)
     ap.add_argument("--temperature", type=float, default=None,
                     help="override the workload's temperature (0 = greedy, no noise)")
-    ap.add_argument("--layout", default="tiled", choices=["rows", "tiled"],
-                    help="W row-major, or repacked once into the tiled matrix-core layout")
+    ap.add_argument("--layout", default="auto", choices=["auto", "rows", "tiled"],
+                    help="W row-major, or repacked once into the tiled matrix-core layout "
+                         "(auto: tiled for bf16 heads, row-major for fp32 ones; the tiled layout is bf16 only)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a device copy of this size (counter calibration) and exit")
     ap.add_argument("--probe", action="store_true",
@@ -246,6 +247,8 @@ def main():
         return
 
     wl = inputs.WORKLOADS[args.workload]
+    if args.layout == "auto":
+        args.layout = "tiled" if wl.dtype == "bf16" else "rows"
     if args.temperature is not None:
         import dataclasses
         wl = dataclasses.replace(wl, temperature=args.temperature)
