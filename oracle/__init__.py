@@ -20,11 +20,15 @@ Modules:
   sampler  exact logits, perturbed scores, the direct sample and its top-2
            margin, and the two-stage tiled form used to pin the partition
            argument.
+  grouped  the grouped (hierarchical) variant: per vocabulary group a local
+           sample and a local log-mass, then a Gumbel-max draw of the group
+           from its own noise stream.
 
 Every function is pinned by a CPU test against something other than itself
 (rocRAND's Philox for the words, closed forms of the Gumbel law, exact
-rational dot products, chi-square against softmax, the T -> 0 limit and
-brute-force argmax over random partitions).
+rational dot products, chi-square against softmax, the T -> 0 limit,
+brute-force argmax over random partitions, and for the grouped variant its
+two index-exact reductions, scipy's logsumexp and chi-square).
 """
 from .philox import philox4x32_10, philox_words, philox4x32_10_scalar  # noqa: F401
 from .gumbel import word_to_uniform, uniform_to_gumbel, gumbel_from_words  # noqa: F401
@@ -36,4 +40,11 @@ from .sampler import (  # noqa: F401
     argmax_lowest,
     sample,
     sample_two_stage,
+)
+from .grouped import (  # noqa: F401
+    GroupedResult,
+    group_noise,
+    group_philox_words,
+    log_mass,
+    sample_grouped,
 )
