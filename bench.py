@@ -77,7 +77,7 @@ def warm(fn, warmup, min_ms):
 
 
 def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, batch_tile=0,
-               single_pass=False, min_warm_ms=0.0):
+               single_pass=False, min_warm_ms=0.0, group_size=0):
     """Returns (ms per step, mean Stage-1 ms, warm-up steps run).
 
     The step time comes from `steps` back-to-back calls bracketed by two
@@ -88,12 +88,13 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
     T, seed = wl.temperature, wl.seed
     tiled = isinstance(Ws[0], fs.TiledWeights)
     ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, variant=variant, vocab_tile=vocab_tile,
-                                        tiled=tiled, single_pass=single_pass), dtype=torch.uint8, device="cuda")
+                                        tiled=tiled, single_pass=single_pass, group_size=group_size),
+                     dtype=torch.uint8, device="cuda")
     if single_pass:
         fs.workspace_reset(ws)
     out = torch.empty(B, dtype=torch.int32, device="cuda")
     kw = dict(out=out, workspace=ws, variant=variant, vocab_tile=vocab_tile, batch_tile=batch_tile,
-              single_pass=single_pass)
+              single_pass=single_pass, group_size=group_size)
     n_warm = warm(lambda i: fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw), warmup, min_warm_ms)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -218,6 +219,8 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="also stream W once per step with the read probe (attainable bandwidth)")
     ap.add_argument("--no-rows", action="store_true", help="skip timing the row-major layout beside")
+    ap.add_argument("--group-size", type=int, default=16384,
+                    help="also time the grouped variant with groups of this many vocab entries (0: skip)")
     ap.add_argument("--single-pass", action="store_true",
                     help="time the one-launch form (Stage 2 folded into Stage 1) as the headline")
     ap.add_argument("--min-warmup-ms", type=float, default=300.0,
@@ -345,6 +348,15 @@ def main():
     result["single_pass" if not single else "two_stage"] = {
         "ms_per_step": other["ms_per_step"], "samples_per_s": other["samples_per_s"],
         "stage1_us": other["stage1_ms"] * 1e3}
+    if args.layout == "tiled" and args.group_size > 0:
+        # the grouped variant (local sample + log-mass per group, group drawn
+        # from the log-masses), groups shaped like vocabulary shards
+        gms, gs1, _ = time_fused(fs, Hd[:B], Ws, wl, args.steps, args.warmup, B, single_pass=False,
+                                 min_warm_ms=args.min_warmup_ms, group_size=args.group_size)
+        result["grouped"] = {"group_size": args.group_size, "n_groups": -(-wl.V // args.group_size),
+                             "ms_per_step": gms, "samples_per_s": B / (gms * 1e-3), "stage1_us": gs1 * 1e3,
+                             "overhead_vs_plain": gms / head["ms_per_step"] - 1.0}
+        log(f"[bench] grouped (G={args.group_size}): {gms * 1e3:.1f} us/step, stage1 {gs1 * 1e3:.1f} us")
     if args.layout == "tiled" and Ws_rows is not None:
         rows = run(B, Ws_rows, single_pass=False)
         result["rows_layout"] = {"ms_per_step": rows["ms_per_step"], "samples_per_s": rows["samples_per_s"],

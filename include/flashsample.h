@@ -99,7 +99,24 @@ typedef struct fs_options {
                               option) must be zero before its first use
                               (fs_workspace_reset), and calls sharing it must
                               not overlap. Results equal the two-stage ones. */
-  int32_t reserved[2];     /* must be 0 */
+  int32_t group_size;      /* > 0: the grouped variant (FlashSampling, arXiv
+                              2603.15854, Section 3, tensor-parallel
+                              paragraphs: a local sample and a local log-mass
+                              per vocabulary group, exact by hierarchical
+                              factorisation). Groups are the contiguous vocab
+                              ranges [k G, (k+1) G); each group's local sample
+                              is its Gumbel-max with the token noise, its
+                              log-mass log sum exp(l/T) over its non-NaN
+                              entries, and the group is drawn by Gumbel-max over
+                              the log-masses with a second Philox stream (counter
+                              word 0 = 0xC0000000 | k >> 2, row, step; word
+                              k & 3). The sample then follows softmax(l/T) but
+                              differs from the plain call's for the same seed.
+                              G must be a multiple of the Stage-1 vocab tile
+                              (any multiple of 256 always is). Bf16 tiled
+                              weights only; not with single_pass. T == 0 gives
+                              the plain greedy result. 0 = plain sampling. */
+  int32_t reserved;        /* must be 0 */
 } fs_options_t;
 
 /* Human-readable name of a status code (static storage). */
@@ -120,8 +137,9 @@ int64_t fs_num_vocab_tiles(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
 int32_t fs_vocab_tile_granule(fs_variant_t variant);
 
 /* Workspace bytes fs_sample_fused needs (candidate buffer of the Stage-1
- * tiles: one 64-bit key per (row, vocab tile); with single_pass, B keys and
- * a counter). 0 on invalid sizes. */
+ * tiles: one 64-bit key per (row, vocab tile); with group_size, also one fp32
+ * log-mass per (row, vocab tile); with single_pass, B keys and a counter).
+ * 0 on invalid sizes or options. */
 size_t fs_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype);
 size_t fs_workspace_bytes_ex(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
                              const fs_options_t* opts);

@@ -50,6 +50,7 @@ struct Plan {
   int32_t batch_tile = 0;
   bool tiled = false;     // W in the tiled layout
   bool single_pass = false;
+  int32_t group_size = 0; // > 0: grouped variant
 };
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
@@ -64,9 +65,19 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   *why = FS_ERR_INVALID_ARGUMENT;
   const int layout = o ? o->weights_layout : FS_LAYOUT_ROWS;
   if (layout != FS_LAYOUT_ROWS && layout != FS_LAYOUT_TILED) return false;
-  if (o && (o->reserved[0] != 0 || o->reserved[1] != 0)) return false;
+  if (o && o->reserved != 0) return false;
+  const int32_t group_size = o ? o->group_size : 0;
+  if (group_size < 0) return false;
   int variant = o ? o->variant : FS_VARIANT_AUTO;
   if (variant != FS_VARIANT_AUTO && variant != FS_VARIANT_GEMV && variant != FS_VARIANT_MFMA) return false;
+  if (group_size > 0) {
+    // the grouped variant: tiled bf16 weights, MFMA kernels, two-stage only
+    if (layout != FS_LAYOUT_TILED || dtype != FS_DTYPE_BF16 || variant == FS_VARIANT_GEMV || (o && o->single_pass)) {
+      *why = FS_ERR_UNSUPPORTED;
+      return false;
+    }
+    variant = FS_VARIANT_MFMA;
+  }
   if (variant == FS_VARIANT_AUTO)
     variant = (dtype == FS_DTYPE_BF16 && B > kGemvMaxB) ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
   int32_t tile = o ? o->vocab_tile : 0;
@@ -99,7 +110,9 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   p->batch_tile = variant == FS_VARIANT_MFMA ? bt : 0;
   p->tiled = layout == FS_LAYOUT_TILED;
   p->single_pass = o && o->single_pass;
+  p->group_size = group_size;
   if (p->n_tiles > 0x7FFFFFFF) return false;
+  if (group_size > 0 && group_size % tile != 0) return false;   // groups are unions of vocab tiles
   return true;
 }
 
@@ -108,9 +121,12 @@ hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, h
   return p.variant == FS_VARIANT_MFMA ? launch_stage1_mfma(a, stream) : launch_stage1_gemv(a, dtype, stream);
 }
 
+size_t cand_bytes(int64_t B, const Plan& p) { return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign); }
+
 size_t fused_ws_bytes(int64_t B, const Plan& p) {
   if (p.single_pass) return align_up((size_t)B * sizeof(uint64_t), kAlign) + kAlign;  // keys + counter
-  return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign);
+  if (p.group_size > 0) return cand_bytes(B, p) + align_up((size_t)B * (size_t)p.n_tiles * sizeof(float), kAlign);
+  return cand_bytes(B, p);
 }
 
 int64_t unfused_ld(int64_t V) { return (V + 7) / 8 * 8; }
@@ -231,6 +247,8 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
 
   Stage1Args a = stage1_args(H, ldh, W, ldw, B, D, V, temperature, seed, step, p);
   a.cand = static_cast<uint64_t*>(workspace);
+  const bool grouped = p.group_size > 0 && !a.greedy;   // greedy: the plain maximiser
+  if (grouped) a.mass = reinterpret_cast<float*>(static_cast<char*>(workspace) + cand_bytes(B, p));
   if (p.single_pass) {
     a.single_pass = 1;
     a.keys = static_cast<uint64_t*>(workspace);
@@ -250,7 +268,10 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
   if (e != hipSuccess) return fail_hip(e);
   if (opts && opts->stage1_stop && (e = hipEventRecord(opts->stage1_stop, stream)) != hipSuccess)
     return fail_hip(e);
-  if (!p.single_pass) {
+  if (grouped) {
+    e = launch_stage2_grouped(a.cand, a.mass, a.B, a.n_tiles, p.group_size / p.tile, a.nk, out_tokens, stream);
+    if (e != hipSuccess) return fail_hip(e);
+  } else if (!p.single_pass) {
     e = launch_stage2(a.cand, a.B, a.n_tiles, out_tokens, stream);
     if (e != hipSuccess) return fail_hip(e);
   }
@@ -279,6 +300,7 @@ fs_status_t fs_sample_unfused_ex(const void* H, int64_t ldh, const void* W, int6
   fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens, opts);
   if (st != FS_OK) return st;
   if (!dtype_ok(logits_dtype)) return FS_ERR_UNSUPPORTED;
+  if (opts && opts->group_size != 0) return FS_ERR_UNSUPPORTED;   // the baseline is plain sampling
   Plan p;
   if (!make_plan(B, D, V, dtype, opts, &p, &st)) return st;
   if (workspace_bytes < unfused_ws_bytes(B, V, logits_dtype)) return FS_ERR_WORKSPACE_TOO_SMALL;

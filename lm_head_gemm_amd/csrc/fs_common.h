@@ -81,6 +81,39 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t x) {
   return -kLn2 * __builtin_amdgcn_logf(e);
 }
 
+// Group stream of the grouped variant: the same key, counter word 0 tagged so
+// it never meets a token counter (those are v >> 2 < 2^29).
+constexpr uint32_t kGroupCounterTag = 0xC0000000u;
+
+__device__ __forceinline__ float group_gumbel(const NoiseKey& nk, uint32_t k, uint32_t b) {
+  const uint4 w = philox4x32_10(make_uint4(kGroupCounterTag | (k >> 2), b, nk.step_lo, nk.step_hi), nk.seed_lo,
+                                nk.seed_hi);
+  return gumbel_from_word(pick_word(w, (int)(k & 3u)));
+}
+
+// ------------------------------------------------------------------ log-mass
+// A partial log-mass is a pair (m, s) standing for s * e^m: m the largest
+// element seen (-inf: none), s the sum of e^(x - m) over the elements (>= 1
+// once one is seen). Merging two pairs rescales to the larger m; the mass is
+// m + ln s. +inf elements make the mass +inf.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -__builtin_inff()) return;   // both empty
+  if (M == __builtin_inff()) {
+    m = M;
+    s = 1.0f;
+    return;
+  }
+  constexpr float kLog2e = 1.4426950408889634f;
+  s = s * __builtin_amdgcn_exp2f((m - M) * kLog2e) + s2 * __builtin_amdgcn_exp2f((m2 - M) * kLog2e);
+  m = M;
+}
+
+__device__ __forceinline__ float lse_value(float m, float s) {
+  constexpr float kLn2 = 0.693147180559945309f;
+  return m == -__builtin_inff() || m == __builtin_inff() ? m : m + kLn2 * __builtin_amdgcn_logf(s);
+}
+
 // ------------------------------------------------------------------ candidate keys
 // A candidate (score s, vocab index v) packs into one 64-bit key whose
 // unsigned order is (s ascending, v descending):
@@ -177,7 +210,8 @@ struct Stage1Args {
   int32_t vocab_tile;   // rows per tile
   int32_t n_tiles;
   int32_t batch_tile;   // MFMA: batch rows per workgroup (0: from B)
-  uint64_t* cand;       // [B, n_tiles] keys, or null (store-only)
+  uint64_t* cand;       // [n_tiles, B] keys, or null (store-only)
+  float* mass;          // [n_tiles, B] tile log-masses of l / T (grouped variant), or null
   void* logits;         // [B, V] logits, or null
   int64_t ld_logits;
   int32_t logits_bf16;  // stored logits dtype
@@ -272,6 +306,8 @@ int64_t tiled_weights_bytes(int64_t V, int64_t D);
 int mfma_tile_rows(int blocks_per_wave);
 hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32_t* out,
                          hipStream_t stream);
+hipError_t launch_stage2_grouped(const uint64_t* cand, const float* mass, int32_t B, int32_t n_tiles,
+                                 int32_t tiles_per_group, NoiseKey nk, int32_t* out, hipStream_t stream);
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,
                                 int32_t V, float inv_t, int32_t greedy, NoiseKey nk,
                                 int32_t part, int32_t n_parts, uint64_t* partial,

@@ -211,6 +211,42 @@ __global__ __launch_bounds__(64 * NW) void gemv_tiled_kernel(Stage1Args a) {
   }
 }
 
+// Tile log-mass (grouped variant). A lane holds N values x = l / T of one
+// batch column (NaN marks an entry past V or a NaN logit, both skipped) and
+// their maximum m; lane_mass adds sum e^(x - m). mass_reduce_store merges the
+// four lanes of the column (q = 0..3) and the q = 0 lane leaves the pair in
+// the workgroup's LDS slot; publish_mass merges the waves' pairs and writes
+// ln(sum e^x) of the tile per batch row to mass[tile, b].
+template <int N>
+__device__ __forceinline__ void lane_mass(const float (&x)[N], float m, float& s) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  s = 0.f;
+  if (m == __builtin_inff()) {
+    s = 1.f;
+  } else if (m != -__builtin_inff()) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (x[i] == x[i]) s += __builtin_amdgcn_exp2f((x[i] - m) * kLog2e);
+  }
+}
+
+__device__ __forceinline__ void mass_reduce_store(float2* slot, int col, int q, float m, float s) {
+  lse_merge(m, s, __shfl_xor(m, 16), __shfl_xor(s, 16));
+  lse_merge(m, s, __shfl_xor(m, 32), __shfl_xor(s, 32));
+  if (q == 0) slot[col] = make_float2(m, s);
+}
+
+template <int NW, int BN>
+__device__ __forceinline__ void publish_mass(const Stage1Args& a, const float2 (&red_mass)[NW][BN], int tile,
+                                             int b0, int n_rows, int tid) {
+  if (tid < n_rows) {
+    float m = -__builtin_inff(), s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) lse_merge(m, s, red_mass[w][tid].x, red_mass[w][tid].y);
+    a.mass[(int64_t)tile * a.B + b0 + tid] = lse_value(m, s);
+  }
+}
+
 // Logits store of the MFMA kernels, staged through LDS. In the accumulator
 // layout lane (r, q) of wave w holds, per 16-column batch block, the logits of
 // vocab rows v_base + 16w + 4q .. +3 for one batch column, so a direct store
@@ -244,7 +280,7 @@ __device__ __forceinline__ void store_logits_staged(const Stage1Args& a, float* 
 }
 
 // ---------------------------------------------------------------- MFMA
-template <int NB, int NW, bool SAMPLE, bool STORE>
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false>
 __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int BN = 16 * NB;
   constexpr int NT = 64 * NW;
@@ -253,6 +289,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
 
   __shared__ uint4 lds_h4[2 * BN * kLdsRow / 8];
   __shared__ uint64_t red[NW][BN];
+  __shared__ float2 red_mass[MASS ? NW : 1][MASS ? BN : 1];
   uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
 
   int vt, bt;
@@ -378,6 +415,16 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
         key = umax64(key, shfl_xor_u64(key, 16));
         key = umax64(key, shfl_xor_u64(key, 32));
         if (q == 0) red[wave][nb * 16 + r] = key;
+        if constexpr (MASS && !kGreedy) {
+          float x[4], mx = -__builtin_inff(), sm = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[j] = (kFull || v0 + j < a.V) ? acc[nb][j] * a.inv_t : __builtin_nanf("");
+            mx = fmaxf(mx, x[j]);   // NaN entries are skipped
+          }
+          lane_mass(x, mx, sm);
+          mass_reduce_store(red_mass[wave], nb * 16 + r, q, mx, sm);
+        }
       }
     };
     const bool full = (int64_t)(vt + 1) * NW * 16 <= a.V;
@@ -395,6 +442,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
 #pragma unroll
       for (int w2 = 1; w2 < NW; ++w2) k = umax64(k, red[w2][tid]);
     }
+    if constexpr (MASS) publish_mass<NW>(a, red_mass, vt, b0, min(BN, a.B - b0), tid);
     publish_candidates(a, vt, b0, min(BN, a.B - b0), k, tid, NT);
   }
 }
@@ -422,7 +470,7 @@ constexpr int kWidePD = 4;                     // W prefetch distance in K steps
 constexpr int kWideBN = 16 * kWideNB;
 constexpr int kWideRows = 16 * kWideNW * kWideMB;
 
-template <bool SAMPLE, bool STORE>
+template <bool SAMPLE, bool STORE, bool MASS = false>
 __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int NB = kWideNB, NW = kWideNW, MB = kWideMB, KSUB = kWideKSub, PD = kWidePD;
   constexpr int BN = kWideBN, NT = 64 * NW, KH = 32 * KSUB, ROW = KH + 16;   // 160-byte rows: conflict-free reads
@@ -433,6 +481,7 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
 
   __shared__ uint4 lds_h4[2 * BN * ROW / 8];
   __shared__ uint64_t red[NW][BN];
+  __shared__ float2 red_mass[MASS ? NW : 1][MASS ? BN : 1];
   uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
 
   int vt, bt;
@@ -591,6 +640,19 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
         key = umax64(key, shfl_xor_u64(key, 16));
         key = umax64(key, shfl_xor_u64(key, 32));
         if (q == 0) red[wave][nb * 16 + r] = key;
+        if constexpr (MASS && !kGreedy) {
+          float x[4 * MB], mx = -__builtin_inff(), sm = 0.f;
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 16 * m[j] + 4 * q + e;
+              x[4 * j + e] = (kFull || v < a.V) ? acc[j][nb][e] * a.inv_t : __builtin_nanf("");
+              mx = fmaxf(mx, x[4 * j + e]);   // NaN entries are skipped
+            }
+          lane_mass(x, mx, sm);
+          mass_reduce_store(red_mass[wave], nb * 16 + r, q, mx, sm);
+        }
       }
     };
     const bool full = (int64_t)(vt + 1) * kWideRows <= a.V;
@@ -608,6 +670,7 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
 #pragma unroll
       for (int w2 = 1; w2 < NW; ++w2) k = umax64(k, red[w2][tid]);
     }
+    if constexpr (MASS) publish_mass<NW>(a, red_mass, vt, b0, min(BN, a.B - b0), tid);
     publish_candidates(a, vt, b0, min(BN, a.B - b0), k, tid, NT);
   }
 }
@@ -648,7 +711,8 @@ hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
   void (*k)(Stage1Args, int32_t) = nullptr;
-  if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true>;
+  if (a.mass) k = store ? mfma_tiled_kernel<NB, NW, true, true, true> : mfma_tiled_kernel<NB, NW, true, false, true>;
+  else if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true>;
   else if (sample) k = mfma_tiled_kernel<NB, NW, true, false>;
   else k = mfma_tiled_kernel<NB, NW, false, true>;
   Stage1Args b = a;
@@ -663,7 +727,8 @@ hipError_t launch_mfma_wide(const Stage1Args& a, hipStream_t stream) {
   const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
   void (*k)(Stage1Args, int32_t) = nullptr;
-  if (sample && store) k = mfma_wide_kernel<true, true>;
+  if (a.mass) k = store ? mfma_wide_kernel<true, true, true> : mfma_wide_kernel<true, false, true>;
+  else if (sample && store) k = mfma_wide_kernel<true, true>;
   else if (sample) k = mfma_wide_kernel<true, false>;
   else k = mfma_wide_kernel<false, true>;
   Stage1Args b = a;

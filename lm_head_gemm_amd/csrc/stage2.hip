@@ -43,6 +43,49 @@ __global__ __launch_bounds__(NT) void stage2_kernel(const uint64_t* __restrict__
   }
 }
 
+// Stage 2 of the grouped variant, one workgroup per batch row: group k is the
+// run of tiles [k tpg, (k+1) tpg). A thread folds each of its groups' tiles
+// into the group's best key (its local sample) and log-mass, scores the group
+// t_k = mass_k + h_k with the group noise, and the workgroup keeps the
+// largest (t_k, lowest k) key; that group's local sample is the token.
+template <int NT>
+__global__ __launch_bounds__(NT) void stage2_grouped_kernel(const uint64_t* __restrict__ cand,
+                                                            const float* __restrict__ mass, int32_t n_tiles,
+                                                            int32_t B, int32_t tpg, NoiseKey nk,
+                                                            int32_t* __restrict__ out) {
+  __shared__ uint64_t red_t[NT];
+  __shared__ uint64_t red_k[NT];
+  const int row = blockIdx.x;
+  const int n_groups = (n_tiles + tpg - 1) / tpg;
+  uint64_t best_t = 0ull, best_key = 0ull;
+  for (int g = threadIdx.x; g < n_groups; g += NT) {
+    uint64_t key = 0ull;
+    float m = -__builtin_inff(), s = 0.f;
+    const int t1 = min(n_tiles, (g + 1) * tpg);
+    for (int t = g * tpg; t < t1; ++t) {
+      key = umax64(key, cand[(int64_t)t * B + row]);
+      lse_merge(m, s, mass[(int64_t)t * B + row], 1.0f);   // e^mass_t as the pair (mass_t, 1)
+    }
+    const float score = lse_value(m, s) + group_gumbel(nk, (uint32_t)g, (uint32_t)row);
+    const uint64_t tk = pack_key(score, (uint32_t)g);
+    if (tk > best_t) {
+      best_t = tk;
+      best_key = key;
+    }
+  }
+  red_t[threadIdx.x] = best_t;
+  red_k[threadIdx.x] = best_key;
+  __syncthreads();
+  for (int w = NT / 2; w >= 1; w >>= 1) {
+    if (threadIdx.x < w && red_t[threadIdx.x + w] > red_t[threadIdx.x]) {
+      red_t[threadIdx.x] = red_t[threadIdx.x + w];
+      red_k[threadIdx.x] = red_k[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[row] = key_to_token(red_k[0]);
+}
+
 // Gumbel-max over materialised logits: workgroup (part, row) scans `part`
 // consecutive vocab entries of one row, four at a time (one Philox call per
 // four), and writes its best key to partial[part, row].
@@ -163,6 +206,12 @@ hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32
                          hipStream_t stream) {
   if (n_tiles <= 4 * 256) return launch(stage2_kernel<256>, dim3(B), dim3(256), 0, stream, cand, n_tiles, B, out);
   return launch(stage2_kernel<1024>, dim3(B), dim3(1024), 0, stream, cand, n_tiles, B, out);
+}
+
+hipError_t launch_stage2_grouped(const uint64_t* cand, const float* mass, int32_t B, int32_t n_tiles,
+                                 int32_t tiles_per_group, NoiseKey nk, int32_t* out, hipStream_t stream) {
+  return launch(stage2_grouped_kernel<256>, dim3(B), dim3(256), 0, stream, cand, mass, n_tiles, B,
+                tiles_per_group, nk, out);
 }
 
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,

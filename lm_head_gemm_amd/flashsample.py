@@ -46,7 +46,8 @@ class FsOptions(ctypes.Structure):
         ("stage1_stop", ctypes.c_void_p),
         ("weights_layout", ctypes.c_int32),
         ("single_pass", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("group_size", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -168,9 +169,10 @@ def _check_inputs(H: torch.Tensor, W):
 
 
 def make_options(variant="auto", vocab_tile=0, logits=None, events=None, batch_tile=0,
-                 layout=FS_LAYOUT_ROWS, single_pass=False) -> FsOptions:
+                 layout=FS_LAYOUT_ROWS, single_pass=False, group_size=0) -> FsOptions:
     o = FsOptions()
     o.single_pass = int(bool(single_pass))
+    o.group_size = int(group_size)
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
     o.vocab_tile = int(vocab_tile)
     o.batch_tile = int(batch_tile)
@@ -197,9 +199,9 @@ def num_vocab_tiles(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0,
 
 
 def workspace_bytes(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0, tiled=False,
-                    single_pass=False) -> int:
+                    single_pass=False, group_size=0) -> int:
     o = make_options(variant, vocab_tile, layout=FS_LAYOUT_TILED if tiled else FS_LAYOUT_ROWS,
-                     single_pass=single_pass)
+                     single_pass=single_pass, group_size=group_size)
     return int(_lib.fs_workspace_bytes_ex(B, D, V, _dtype_code(dtype), ctypes.byref(o)))
 
 
@@ -210,14 +212,18 @@ def unfused_workspace_bytes(B, D, V, dtype=torch.bfloat16, logits_dtype=torch.bf
 def sample_fused(H: torch.Tensor, W, temperature: float, seed: int, step: int,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                  variant="auto", vocab_tile: int = 0, logits: torch.Tensor | None = None,
-                 events=None, stream=None, batch_tile: int = 0, single_pass: bool = False) -> torch.Tensor:
+                 events=None, stream=None, batch_tile: int = 0, single_pass: bool = False,
+                 group_size: int = 0) -> torch.Tensor:
     """One token per row of H from softmax(H W^T / T) (Gumbel-max, fused).
     W is a row-major [V, D] tensor or a TiledWeights. With single_pass, a
-    caller-provided workspace must have been zeroed once (workspace_reset)."""
+    caller-provided workspace must have been zeroed once (workspace_reset).
+    group_size > 0 selects the grouped variant (tiled weights only): the
+    group of group_size vocab entries is drawn from its log-mass, the token
+    is that group's local Gumbel-max sample."""
     _check_inputs(H, W)
     B, D = H.shape
     wptr, ldw, V, _, layout = _weights(W)
-    o = make_options(variant, vocab_tile, logits, events, batch_tile, layout, single_pass)
+    o = make_options(variant, vocab_tile, logits, events, batch_tile, layout, single_pass, group_size)
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=H.device)
     if workspace is None:

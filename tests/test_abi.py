@@ -160,7 +160,7 @@ def test_tiled_layout_validation(lib):
     o.weights_layout = 2
     assert _fused(lib, opts=o) == INVALID
     o = FsOptions()
-    o.reserved[1] = 1
+    o.reserved = 1
     assert _fused(lib, opts=o) == INVALID
     # single pass: B keys + a counter, independent of the tile count
     o = FsOptions()
@@ -202,3 +202,35 @@ def test_tiled_layout_validation(lib):
     o = FsOptions()
     o.weights_layout = 3
     assert lib.fs_sample_unfused_ex(*base, ctypes.byref(o)) == INVALID
+
+
+def test_grouped_option_validation(lib):
+    """group_size: tiled bf16 MFMA, two-stage only, a multiple of the vocab tile;
+    the workspace adds one fp32 log-mass per (tile, row)."""
+    from lm_head_gemm_amd.flashsample import FsOptions
+    o = FsOptions()
+    o.weights_layout = 1
+    o.group_size = -256
+    assert _fused(lib, opts=o) == INVALID
+    o.group_size = 256
+    nt = lib.fs_num_vocab_tiles(8, 4096, 128256, BF16, ctypes.byref(o))
+    assert nt == 1002  # MFMA default tile 128 below B = 65
+    want = -(-8 * nt * 8 // 256) * 256 + -(-8 * nt * 4 // 256) * 256
+    assert lib.fs_workspace_bytes_ex(8, 4096, 128256, BF16, ctypes.byref(o)) == want
+    o.group_size = 192            # not a multiple of the 128-row tile
+    assert lib.fs_workspace_bytes_ex(8, 4096, 128256, BF16, ctypes.byref(o)) == 0
+    assert _fused(lib, opts=o) == INVALID
+    o.group_size = 128
+    assert lib.fs_workspace_bytes_ex(100, 4096, 128256, BF16, ctypes.byref(o)) == 0  # wide tile is 256
+    o.group_size = 256
+    o.single_pass = 1
+    assert _fused(lib, opts=o) == UNSUPPORTED
+    o.single_pass = 0
+    o.variant = 1                 # GEMV
+    assert _fused(lib, opts=o) == UNSUPPORTED
+    o = FsOptions()               # row-major W
+    o.group_size = 256
+    assert _fused(lib, opts=o) == UNSUPPORTED
+    base = [FAKE, 64, FAKE, 64, BF16, 2, 64, 1000, 1.0, 0, 0, F32, FAKE, 1 << 20, FAKE, None]
+    o.weights_layout = 1
+    assert lib.fs_sample_unfused_ex(*base, ctypes.byref(o)) == UNSUPPORTED
