@@ -43,47 +43,72 @@ __global__ __launch_bounds__(NT) void stage2_kernel(const uint64_t* __restrict__
   }
 }
 
-// Stage 2 of the grouped variant, one workgroup per batch row: group k is the
-// run of tiles [k tpg, (k+1) tpg). A thread folds each of its groups' tiles
-// into the group's best key (its local sample) and log-mass, scores the group
-// t_k = mass_k + h_k with the group noise, and the workgroup keeps the
-// largest (t_k, lowest k) key; that group's local sample is the token.
+// Stage 2 of the grouped variant, one workgroup per batch row: group g is the
+// run of tiles [g tpg, (g+1) tpg). Each group's tiles are folded into its best
+// key (the local sample) and log-mass; the group is scored t_g = mass_g + h_g
+// with the group noise, and the largest (t_g, lowest g) key wins; that
+// group's local sample is the token. Few large groups (tpg >= 16): a wave per
+// group, lanes over its tiles, shuffle reductions. Many small groups: a
+// thread per group, walking its tiles.
 template <int NT>
 __global__ __launch_bounds__(NT) void stage2_grouped_kernel(const uint64_t* __restrict__ cand,
                                                             const float* __restrict__ mass, int32_t n_tiles,
                                                             int32_t B, int32_t tpg, NoiseKey nk,
                                                             int32_t* __restrict__ out) {
+  constexpr int NW = NT / 64;
   __shared__ uint64_t red_t[NT];
   __shared__ uint64_t red_k[NT];
   const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_groups = (n_tiles + tpg - 1) / tpg;
   uint64_t best_t = 0ull, best_key = 0ull;
-  for (int g = threadIdx.x; g < n_groups; g += NT) {
-    uint64_t key = 0ull;
-    float m = -__builtin_inff(), s = 0.f;
-    const int t1 = min(n_tiles, (g + 1) * tpg);
-    for (int t = g * tpg; t < t1; ++t) {
-      key = umax64(key, cand[(int64_t)t * B + row]);
-      lse_merge(m, s, mass[(int64_t)t * B + row], 1.0f);   // e^mass_t as the pair (mass_t, 1)
-    }
+  auto score_group = [&](int g, uint64_t key, float m, float s) {
     const float score = lse_value(m, s) + group_gumbel(nk, (uint32_t)g, (uint32_t)row);
     const uint64_t tk = pack_key(score, (uint32_t)g);
     if (tk > best_t) {
       best_t = tk;
       best_key = key;
     }
+  };
+  if (tpg >= 16) {
+    for (int g = wave; g < n_groups; g += NW) {   // uniform per wave
+      const int t1 = min(n_tiles, (g + 1) * tpg);
+      uint64_t key = 0ull;
+      float m = -__builtin_inff(), s = 0.f;
+      for (int t = g * tpg + lane; t < t1; t += 64) {
+        key = umax64(key, cand[(int64_t)t * B + row]);
+        lse_merge(m, s, mass[(int64_t)t * B + row], 1.0f);   // e^mass_t as the pair (mass_t, 1)
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        key = umax64(key, shfl_xor_u64(key, off));
+        lse_merge(m, s, __shfl_xor(m, off), __shfl_xor(s, off));
+      }
+      if (lane == 0) score_group(g, key, m, s);
+    }
+  } else {
+    for (int g = tid; g < n_groups; g += NT) {
+      const int t1 = min(n_tiles, (g + 1) * tpg);
+      uint64_t key = 0ull;
+      float m = -__builtin_inff(), s = 0.f;
+      for (int t = g * tpg; t < t1; ++t) {
+        key = umax64(key, cand[(int64_t)t * B + row]);
+        lse_merge(m, s, mass[(int64_t)t * B + row], 1.0f);
+      }
+      score_group(g, key, m, s);
+    }
   }
-  red_t[threadIdx.x] = best_t;
-  red_k[threadIdx.x] = best_key;
+  red_t[tid] = best_t;
+  red_k[tid] = best_key;
   __syncthreads();
   for (int w = NT / 2; w >= 1; w >>= 1) {
-    if (threadIdx.x < w && red_t[threadIdx.x + w] > red_t[threadIdx.x]) {
-      red_t[threadIdx.x] = red_t[threadIdx.x + w];
-      red_k[threadIdx.x] = red_k[threadIdx.x + w];
+    if (tid < w && red_t[tid + w] > red_t[tid]) {
+      red_t[tid] = red_t[tid + w];
+      red_k[tid] = red_k[tid + w];
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[row] = key_to_token(red_k[0]);
+  if (tid == 0) out[row] = key_to_token(red_k[0]);
 }
 
 // Gumbel-max over materialised logits: workgroup (part, row) scans `part`
