@@ -29,7 +29,10 @@
  *  - H is row-major [B, D] with row stride ldh elements, W row-major [V, D]
  *    with row stride ldw elements (ld >= D). Both have the same dtype.
  *    Base pointers must be 16-byte aligned and ld * sizeof(dtype) and
- *    D * sizeof(dtype) multiples of 16 (else FS_ERR_UNSUPPORTED).
+ *    D * sizeof(dtype) multiples of 16 (else FS_ERR_UNSUPPORTED). One H row
+ *    must fit the on-chip LDS beside the kernels' own reduction arrays:
+ *    D * sizeof(dtype) <= 159 KiB (D <= 81408 bf16, 40704 fp32; else
+ *    FS_ERR_UNSUPPORTED).
  *  - Calls are asynchronous on `stream`: they validate, enqueue and return.
  *    Only the workspace and the outputs are written. Distinct calls may run
  *    concurrently if they use distinct workspaces and outputs.

@@ -27,6 +27,9 @@ constexpr int32_t kMfmaLargeBTile = 128;    // two blocks per wave above 32 rows
 constexpr int64_t kGemvMaxB = 2;            // bf16 batches above this use the MFMA kernel
 constexpr int32_t kSamplePart = 2048;       // unfused sampler: vocab entries per workgroup
 constexpr size_t kAlign = 256;
+// The GEMV kernels stage whole H rows in LDS (160 KiB per workgroup) next to
+// their own reduction arrays (under 1 KiB).
+constexpr int64_t kMaxHRowBytes = 159 * 1024;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -157,7 +160,7 @@ fs_status_t check_common(const void* H, int64_t ldh, const void* W, int64_t ldw,
   const int64_t esz = (int64_t)dtype_size((fs_dtype_t)dtype);
   if (!aligned16(H) || !aligned16(W) || !aligned16(ws)) return FS_ERR_UNSUPPORTED;
   if ((D * esz) % 16 || (ldh * esz) % 16 || (ldw * esz) % 16) return FS_ERR_UNSUPPORTED;
-  if (D * esz > 160 * 1024) return FS_ERR_UNSUPPORTED;  // one H row must fit LDS
+  if (D * esz > kMaxHRowBytes) return FS_ERR_UNSUPPORTED;  // one H row must fit LDS
   return FS_OK;
 }
 

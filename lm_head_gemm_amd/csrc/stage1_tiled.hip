@@ -46,6 +46,7 @@ constexpr int kBlock16 = kKS * 64;  // 16-byte pieces per block
 constexpr int kLdsRow = kBK + 16;
 constexpr int kXcds = 8;
 constexpr int kGroup = 8;           // row blocks per group in the tiled layout
+constexpr int64_t kMaxHLds = 159 * 1024;  // LDS bytes for staged H rows (the rest: reduction arrays)
 
 // First 16-byte piece of block (m, c) of the tiled layout.
 __device__ __forceinline__ int64_t block_piece(int m, int c, int nC) {
@@ -696,7 +697,8 @@ hipError_t launch_gemv_bb(const Stage1Args& a, hipStream_t stream) {
 
 template <int NW>
 hipError_t launch_gemv_nw(const Stage1Args& a, hipStream_t stream) {
-  const int bb = a.B <= 1 ? 1 : a.B <= 2 ? 2 : 4;
+  int bb = a.B <= 1 ? 1 : a.B <= 2 ? 2 : 4;
+  while (bb > 1 && (int64_t)bb * a.D * 2 > kMaxHLds) bb /= 2;   // BB rows of H must fit the LDS
   if (bb == 1) return launch_gemv_bb<1, NW>(a, stream);
   if (bb == 2) return launch_gemv_bb<2, NW>(a, stream);
   return launch_gemv_bb<4, NW>(a, stream);

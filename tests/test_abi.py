@@ -94,6 +94,7 @@ def _fused(lib, **kw):
     (dict(H=FAKE + 2), UNSUPPORTED), (dict(W=FAKE + 8), UNSUPPORTED), (dict(ws=FAKE + 4), UNSUPPORTED),
     (dict(D=12, ldh=12, ldw=12), UNSUPPORTED), (dict(ldh=68), UNSUPPORTED),
     (dict(D=128 * 1024, ldh=128 * 1024, ldw=128 * 1024), UNSUPPORTED),
+    (dict(D=81416, ldh=81416, ldw=81416), UNSUPPORTED),   # H row past 159 KiB
     (dict(wsb=8), WS_SMALL),
 ])
 def test_fused_validation(lib, kw, status):
