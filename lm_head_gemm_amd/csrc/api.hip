@@ -121,7 +121,10 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
 
 hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream) {
   if (p.tiled) return launch_stage1_tiled(a, p.variant == FS_VARIANT_MFMA, stream);
-  return p.variant == FS_VARIANT_MFMA ? launch_stage1_mfma(a, stream) : launch_stage1_gemv(a, dtype, stream);
+  if (p.variant != FS_VARIANT_MFMA) return launch_stage1_gemv(a, dtype, stream);
+  // row-major MFMA: the A operand straight from the rows when D is a multiple
+  // of the K block, else the kernel that transposes W through LDS
+  return rows_direct_ok(a) ? launch_stage1_rows_direct(a, stream) : launch_stage1_mfma(a, stream);
 }
 
 size_t cand_bytes(int64_t B, const Plan& p) { return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign); }

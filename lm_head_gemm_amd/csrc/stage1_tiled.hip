@@ -281,7 +281,11 @@ __device__ __forceinline__ void store_logits_staged(const Stage1Args& a, float* 
 }
 
 // ---------------------------------------------------------------- MFMA
-template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false>
+// ROWS: W is row-major [V, D] (stride ldw, D a multiple of 256) instead of
+// tiled; each lane then loads its A-operand piece straight from its row,
+// W[16m + r][256c + 32t + 8q .. +8], rows past V clamped to the last row
+// (their candidates are never valid).
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false, bool ROWS = false>
 __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int BN = 16 * NB;
   constexpr int NT = 64 * NW;
@@ -307,7 +311,15 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   const int nM = (a.V + 15) / 16;
   const int m = vt * NW + wave;
   const int mc = min(m, nM - 1);
+  // first 16-byte piece of this lane in K block c; K step t is kTStride further
+  constexpr int kTStride = ROWS ? 4 : 64;
+  const uint4* wrow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.W) +
+                                                     (int64_t)min(16 * mc + r, a.V - 1) * a.ldw + 8 * q);
   const uint4* wt = static_cast<const uint4*>(a.W) + lane;
+  auto wblock = [&](int c) { return ROWS ? wrow + c * (kBK / 8) : wt + block_piece(mc, c, nC); };
+  // tiled: non-temporal (read once); rows: cached, so the second half of each
+  // 128-byte line (the next K step's pieces) is served by the first's fetch
+  auto wload = [&](const uint4* p) { return ROWS ? *p : load_stream16(p); };
   const uint16_t* H = static_cast<const uint16_t*>(a.H);
 
   // This thread's share of each H block: rows hn[i], columns hk[i] .. +8;
@@ -347,9 +359,9 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   uint4 w[kKS];
   uint4 hreg[HP];
   {
-    const uint4* p = wt + block_piece(mc, 0, nC);
+    const uint4* p = wblock(0);
 #pragma unroll
-    for (int t = 0; t < kKS; ++t) w[t] = load_stream16(p + t * 64);
+    for (int t = 0; t < kKS; ++t) w[t] = wload(p + t * kTStride);
   }
   load_h(0, hreg);
   store_h(0, hreg);
@@ -359,12 +371,12 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   // The last block is peeled off so no load is ever issued for nothing.
   auto step = [&](int c, bool more) {
     if (more) load_h(c + 1, hreg);
-    const uint4* p = wt + block_piece(mc, more ? c + 1 : c, nC);
+    const uint4* p = wblock(more ? c + 1 : c);
     const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow;
 #pragma unroll
     for (int t = 0; t < kKS; ++t) {
       const uint4 x = w[t];
-      if (more) w[t] = load_stream16(p + t * 64);
+      if (more) w[t] = wload(p + t * kTStride);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
@@ -704,7 +716,7 @@ hipError_t launch_gemv_nw(const Stage1Args& a, hipStream_t stream) {
   return launch_gemv_bb<4, NW>(a, stream);
 }
 
-template <int NB, int NW>
+template <int NB, int NW, bool ROWS>
 hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   constexpr int BN = 16 * NB;
   const bool sample = a.cand != nullptr;
@@ -713,10 +725,11 @@ hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
   void (*k)(Stage1Args, int32_t) = nullptr;
-  if (a.mass) k = store ? mfma_tiled_kernel<NB, NW, true, true, true> : mfma_tiled_kernel<NB, NW, true, false, true>;
-  else if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true>;
-  else if (sample) k = mfma_tiled_kernel<NB, NW, true, false>;
-  else k = mfma_tiled_kernel<NB, NW, false, true>;
+  if (a.mass && !ROWS)
+    k = store ? mfma_tiled_kernel<NB, NW, true, true, true> : mfma_tiled_kernel<NB, NW, true, false, true>;
+  else if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true, false, ROWS>;
+  else if (sample) k = mfma_tiled_kernel<NB, NW, true, false, false, ROWS>;
+  else k = mfma_tiled_kernel<NB, NW, false, true, false, ROWS>;
   Stage1Args b = a;
   b.total_wgs = (int32_t)G;
   return launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b, (int32_t)n_bt);
@@ -738,12 +751,12 @@ hipError_t launch_mfma_wide(const Stage1Args& a, hipStream_t stream) {
   return launch(k, dim3((unsigned)grid), dim3(64 * kWideNW), 0, stream, b, (int32_t)n_bt);
 }
 
-template <int NW>
+template <int NW, bool ROWS = false>
 hipError_t launch_mfma_nw(const Stage1Args& a, hipStream_t stream) {
   const int bn = a.batch_tile ? a.batch_tile : (a.B <= 16 ? 16 : a.B <= 32 ? 32 : 64);
-  if (bn == 16) return launch_mfma_nb<1, NW>(a, stream);
-  if (bn == 32) return launch_mfma_nb<2, NW>(a, stream);
-  return launch_mfma_nb<4, NW>(a, stream);
+  if (bn == 16) return launch_mfma_nb<1, NW, ROWS>(a, stream);
+  if (bn == 32) return launch_mfma_nb<2, NW, ROWS>(a, stream);
+  return launch_mfma_nb<4, NW, ROWS>(a, stream);
 }
 
 }  // namespace
@@ -759,6 +772,16 @@ hipError_t launch_pack_tiled(const void* W, int64_t ldw, int32_t V, int32_t D, v
   const dim3 grid((unsigned)((n16 + 255) / 256));
   return launch(pack_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(W), ldw, V, D, nC, n16,
                 static_cast<uint4*>(out));
+}
+
+// Row-major bf16 W with D a multiple of 256, MFMA: the narrow kernel reading
+// its A operand straight from the rows (vocab tile 64 or 128 = 4 or 8 waves).
+bool rows_direct_ok(const Stage1Args& a) {
+  return a.D % kBK == 0 && (a.vocab_tile == 64 || a.vocab_tile == 128) && a.mass == nullptr;
+}
+
+hipError_t launch_stage1_rows_direct(const Stage1Args& a, hipStream_t stream) {
+  return a.vocab_tile == 128 ? launch_mfma_nw<8, true>(a, stream) : launch_mfma_nw<4, true>(a, stream);
 }
 
 // Vocab tile = 16 rows per wave x waves per workgroup (4 or 8), or the
