@@ -78,10 +78,11 @@ typedef struct fs_options {
   int32_t variant;         /* fs_variant_t */
   int32_t vocab_tile;      /* rows per Stage-1 vocab tile; 0 = variant default.
                               Row-major W: a multiple of the variant's granule
-                              (fs_vocab_tile_granule). Tiled W: 64 or 128, or
-                              256 for MFMA (the wide kernel: 8 waves of two
-                              16-row blocks, 128-column batch tiles; the
-                              default from B = 65 on). */
+                              (fs_vocab_tile_granule); MFMA: 64 or 128, or 256
+                              when D is a multiple of 256. Tiled W: 64 or 128,
+                              or 256 for MFMA. 256 is the wide kernel (8 waves
+                              of two 16-row blocks, 128-column batch tiles; the
+                              default from B = 65 on where allowed). */
   void* logits;            /* non-null: the fused call also stores l = H W^T
                               (device [B, V] row-major, stride ld_logits) */
   int64_t ld_logits;
@@ -116,9 +117,10 @@ typedef struct fs_options {
                               k & 3). The sample then follows softmax(l/T) but
                               differs from the plain call's for the same seed.
                               G must be a multiple of the Stage-1 vocab tile
-                              (any multiple of 256 always is). Bf16 tiled
-                              weights only; not with single_pass. T == 0 gives
-                              the plain greedy result. 0 = plain sampling. */
+                              (any multiple of 256 always is). Bf16, tiled
+                              weights or row-major ones with D a multiple of
+                              256; not with single_pass. T == 0 gives the plain
+                              greedy result. 0 = plain sampling. */
   int32_t reserved;        /* must be 0 */
 } fs_options_t;
 

@@ -64,7 +64,6 @@ struct Plan {
 //     256-row wide tile (8 waves of two blocks, batch tile 128).
 bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* o, Plan* p,
                fs_status_t* why) {
-  (void)D;
   *why = FS_ERR_INVALID_ARGUMENT;
   const int layout = o ? o->weights_layout : FS_LAYOUT_ROWS;
   if (layout != FS_LAYOUT_ROWS && layout != FS_LAYOUT_TILED) return false;
@@ -74,8 +73,10 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   int variant = o ? o->variant : FS_VARIANT_AUTO;
   if (variant != FS_VARIANT_AUTO && variant != FS_VARIANT_GEMV && variant != FS_VARIANT_MFMA) return false;
   if (group_size > 0) {
-    // the grouped variant: tiled bf16 weights, MFMA kernels, two-stage only
-    if (layout != FS_LAYOUT_TILED || dtype != FS_DTYPE_BF16 || variant == FS_VARIANT_GEMV || (o && o->single_pass)) {
+    // the grouped variant: bf16, tiled weights or row-major ones with D a
+    // multiple of 256 (the kernels with the log-mass epilogue), MFMA, two-stage
+    const bool direct_ok = layout == FS_LAYOUT_TILED || rows_direct_ok(D);   // kernels with the log-mass epilogue
+    if (!direct_ok || dtype != FS_DTYPE_BF16 || variant == FS_VARIANT_GEMV || (o && o->single_pass)) {
       *why = FS_ERR_UNSUPPORTED;
       return false;
     }
@@ -101,8 +102,13 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
       *why = FS_ERR_UNSUPPORTED;
       return false;
     }
-    if (tile == 0) tile = B > 32 ? kMfmaLargeBTile : kMfmaSmallBTile;
-    if (tile != mfma_tile_rows(1) && tile != mfma_tile_rows(2)) return false;
+    // D a multiple of 256: the tiled-layout kernels read the rows directly,
+    // the 256-row wide tile included; other D: the transposing kernel
+    const bool direct = rows_direct_ok(D);
+    if (tile == 0) tile = direct && B >= kTiledWideMinB ? kTiledWideTile : B > 32 ? kMfmaLargeBTile : kMfmaSmallBTile;
+    const bool wide = direct && tile == kTiledWideTile;
+    if (tile != mfma_tile_rows(1) && tile != mfma_tile_rows(2) && !wide) return false;
+    if (wide != (bt == kTiledWideBatch) && bt != 0) return false;
   } else {
     if (tile == 0) tile = kGemvDefaultTile;
     if (tile < 0 || tile % kGemvGranule != 0) return false;
@@ -124,7 +130,7 @@ hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, h
   if (p.variant != FS_VARIANT_MFMA) return launch_stage1_gemv(a, dtype, stream);
   // row-major MFMA: the A operand straight from the rows when D is a multiple
   // of the K block, else the kernel that transposes W through LDS
-  return rows_direct_ok(a) ? launch_stage1_rows_direct(a, stream) : launch_stage1_mfma(a, stream);
+  return rows_direct_ok(a.D) ? launch_stage1_rows_direct(a, stream) : launch_stage1_mfma(a, stream);
 }
 
 size_t cand_bytes(int64_t B, const Plan& p) { return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign); }

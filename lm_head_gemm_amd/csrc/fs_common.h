@@ -301,7 +301,7 @@ hipError_t launch_stage1_gemv(const Stage1Args& a, fs_dtype_t dtype, hipStream_t
 int gemv_batch_tile(int64_t B, int64_t D, fs_dtype_t dtype);
 hipError_t launch_stage1_mfma(const Stage1Args& a, hipStream_t stream);
 hipError_t launch_stage1_tiled(const Stage1Args& a, bool mfma, hipStream_t stream);
-bool rows_direct_ok(const Stage1Args& a);
+bool rows_direct_ok(int64_t D);
 hipError_t launch_stage1_rows_direct(const Stage1Args& a, hipStream_t stream);
 hipError_t launch_pack_tiled(const void* W, int64_t ldw, int32_t V, int32_t D, void* out, hipStream_t stream);
 int64_t tiled_weights_bytes(int64_t V, int64_t D);

@@ -483,7 +483,10 @@ constexpr int kWidePD = 4;                     // W prefetch distance in K steps
 constexpr int kWideBN = 16 * kWideNB;
 constexpr int kWideRows = 16 * kWideNW * kWideMB;
 
-template <bool SAMPLE, bool STORE, bool MASS = false>
+// ROWS: row-major W [V, D] (D a multiple of 256) read directly, as in the
+// 16-rows-per-wave kernel: lane (r, q) of row block m loads
+// W[16m + r][256c + 32t + 8q .. +8], rows past V clamped.
+template <bool SAMPLE, bool STORE, bool MASS = false, bool ROWS = false>
 __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int NB = kWideNB, NW = kWideNW, MB = kWideMB, KSUB = kWideKSub, PD = kWidePD;
   constexpr int BN = kWideBN, NT = 64 * NW, KH = 32 * KSUB, ROW = KH + 16;   // 160-byte rows: conflict-free reads
@@ -516,6 +519,15 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
     mc[j] = min(m[j], nM - 1);
   }
   const uint4* wt = static_cast<const uint4*>(a.W) + lane;
+  const uint4* wrow[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+    wrow[j] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.W) +
+                                             (int64_t)min(16 * mc[j] + r, a.V - 1) * a.ldw + 8 * q);
+  // 16-byte piece of this lane for row block j, K block c, K step t
+  auto wpiece = [&](int j, int c, int t) {
+    return ROWS ? wrow[j][c * (kBK / 8) + 4 * t] : wt[block_piece(mc[j], c, nC) + t * 64];
+  };
   const uint16_t* H = static_cast<const uint16_t*>(a.H);
 
   int hn[HP], hk[HP];
@@ -563,7 +575,7 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
 #pragma unroll
   for (int j = 0; j < MB; ++j)
 #pragma unroll
-    for (int t = 0; t < PD; ++t) w[j][t] = wt[block_piece(mc[j], 0, nC) + t * 64];
+    for (int t = 0; t < PD; ++t) w[j][t] = wpiece(j, 0, t);
   load_h(0, hreg);
   store_h(0, hreg);
   __syncthreads();
@@ -589,7 +601,7 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
 #pragma unroll
         for (int j = 0; j < MB; ++j) {
           x[j] = w[j][t % PD];
-          if (refill) w[j][t % PD] = wt[block_piece(mc[j], cn, nC) + (tn % kKS) * 64];
+          if (refill) w[j][t % PD] = wpiece(j, cn, tn % kKS);
         }
         if (tt + 1 < KSUB) {
           read_b(buf, tt + 1, bf[(tt + 1) & 1]);
@@ -725,8 +737,8 @@ hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
   void (*k)(Stage1Args, int32_t) = nullptr;
-  if (a.mass && !ROWS)
-    k = store ? mfma_tiled_kernel<NB, NW, true, true, true> : mfma_tiled_kernel<NB, NW, true, false, true>;
+  if (a.mass)
+    k = store ? mfma_tiled_kernel<NB, NW, true, true, true, ROWS> : mfma_tiled_kernel<NB, NW, true, false, true, ROWS>;
   else if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true, false, ROWS>;
   else if (sample) k = mfma_tiled_kernel<NB, NW, true, false, false, ROWS>;
   else k = mfma_tiled_kernel<NB, NW, false, true, false, ROWS>;
@@ -735,6 +747,7 @@ hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   return launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b, (int32_t)n_bt);
 }
 
+template <bool ROWS>
 hipError_t launch_mfma_wide(const Stage1Args& a, hipStream_t stream) {
   const bool sample = a.cand != nullptr;
   const bool store = a.logits != nullptr;
@@ -742,10 +755,10 @@ hipError_t launch_mfma_wide(const Stage1Args& a, hipStream_t stream) {
   const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
   void (*k)(Stage1Args, int32_t) = nullptr;
-  if (a.mass) k = store ? mfma_wide_kernel<true, true, true> : mfma_wide_kernel<true, false, true>;
-  else if (sample && store) k = mfma_wide_kernel<true, true>;
-  else if (sample) k = mfma_wide_kernel<true, false>;
-  else k = mfma_wide_kernel<false, true>;
+  if (a.mass) k = store ? mfma_wide_kernel<true, true, true, ROWS> : mfma_wide_kernel<true, false, true, ROWS>;
+  else if (sample && store) k = mfma_wide_kernel<true, true, false, ROWS>;
+  else if (sample) k = mfma_wide_kernel<true, false, false, ROWS>;
+  else k = mfma_wide_kernel<false, true, false, ROWS>;
   Stage1Args b = a;
   b.total_wgs = (int32_t)G;
   return launch(k, dim3((unsigned)grid), dim3(64 * kWideNW), 0, stream, b, (int32_t)n_bt);
@@ -774,20 +787,20 @@ hipError_t launch_pack_tiled(const void* W, int64_t ldw, int32_t V, int32_t D, v
                 static_cast<uint4*>(out));
 }
 
-// Row-major bf16 W with D a multiple of 256, MFMA: the narrow kernel reading
-// its A operand straight from the rows (vocab tile 64 or 128 = 4 or 8 waves).
-bool rows_direct_ok(const Stage1Args& a) {
-  return a.D % kBK == 0 && (a.vocab_tile == 64 || a.vocab_tile == 128) && a.mass == nullptr;
-}
+// Row-major bf16 W with D a multiple of 256, MFMA: the tiled-layout MFMA
+// kernels reading their A operand straight from the rows (vocab tile 64 or
+// 128 = 4 or 8 waves of one row block; 256 = the wide kernel).
+bool rows_direct_ok(int64_t D) { return D % kBK == 0; }
 
 hipError_t launch_stage1_rows_direct(const Stage1Args& a, hipStream_t stream) {
+  if (a.vocab_tile == kWideRows) return launch_mfma_wide<true>(a, stream);
   return a.vocab_tile == 128 ? launch_mfma_nw<8, true>(a, stream) : launch_mfma_nw<4, true>(a, stream);
 }
 
 // Vocab tile = 16 rows per wave x waves per workgroup (4 or 8), or the
 // 256-row wide tile (8 waves x 2 row blocks, MFMA only).
 hipError_t launch_stage1_tiled(const Stage1Args& a, bool mfma, hipStream_t stream) {
-  if (mfma && a.vocab_tile == kWideRows) return launch_mfma_wide(a, stream);
+  if (mfma && a.vocab_tile == kWideRows) return launch_mfma_wide<false>(a, stream);
   const bool eight = a.vocab_tile == 128;
   if (mfma) return eight ? launch_mfma_nw<8>(a, stream) : launch_mfma_nw<4>(a, stream);
   return eight ? launch_gemv_nw<8>(a, stream) : launch_gemv_nw<4>(a, stream);

@@ -217,9 +217,10 @@ def sample_fused(H: torch.Tensor, W, temperature: float, seed: int, step: int,
     """One token per row of H from softmax(H W^T / T) (Gumbel-max, fused).
     W is a row-major [V, D] tensor or a TiledWeights. With single_pass, a
     caller-provided workspace must have been zeroed once (workspace_reset).
-    group_size > 0 selects the grouped variant (tiled weights only): the
-    group of group_size vocab entries is drawn from its log-mass, the token
-    is that group's local Gumbel-max sample."""
+    group_size > 0 selects the grouped variant (bf16; tiled weights, or
+    row-major ones with D a multiple of 256): the group of group_size vocab
+    entries is drawn from its log-mass, the token is that group's local
+    Gumbel-max sample."""
     _check_inputs(H, W)
     B, D = H.shape
     wptr, ldw, V, _, layout = _weights(W)

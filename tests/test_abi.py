@@ -229,9 +229,13 @@ def test_grouped_option_validation(lib):
     o.single_pass = 0
     o.variant = 1                 # GEMV
     assert _fused(lib, opts=o) == UNSUPPORTED
-    o = FsOptions()               # row-major W
+    o = FsOptions()               # row-major W: only with D a multiple of 256
     o.group_size = 256
     assert _fused(lib, opts=o) == UNSUPPORTED
+    assert _fused(lib, opts=o, D=256, ldh=256, ldw=256, wsb=8) == WS_SMALL
+    assert lib.fs_num_vocab_tiles(100, 512, 5000, BF16, ctypes.byref(o)) == 20   # wide tile from B = 65
+    o.vocab_tile = 256
+    assert lib.fs_num_vocab_tiles(100, 520, 5000, BF16, ctypes.byref(o)) == -1   # not for other D
     base = [FAKE, 64, FAKE, 64, BF16, 2, 64, 1000, 1.0, 0, 0, F32, FAKE, 1 << 20, FAKE, None]
     o.weights_layout = 1
     assert lib.fs_sample_unfused_ex(*base, ctypes.byref(o)) == UNSUPPORTED

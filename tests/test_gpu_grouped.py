@@ -120,3 +120,15 @@ def test_grouped_full_size_sampled_rows(fs, name, B, G):
     rows = np.unique(np.concatenate([[0, B - 1], np.random.default_rng(wl.seed).choice(B, 6, replace=False)]))
     n, near = check_grouped_parity(H, W, wl.temperature, wl.seed, 3, G, rows, tok[rows])
     print(f"{name} B={B} G={G}: {n} rows checked, {near} near ties")
+
+
+@pytest.mark.parametrize("tile,G", [(64, 128), (128, 256), (256, 512)])
+@pytest.mark.parametrize("B,D,V", [(3, 256, 1000), (40, 512, 3001), (150, 256, 2053)])
+def test_grouped_parity_row_major(fs, tile, G, B, D, V):
+    """Row-major W with D a multiple of 256: the MFMA kernels read the rows
+    directly and carry the same log-mass epilogue."""
+    H, W = _rand_head(B * 17 + D + V + G, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    for T, seed, step in ((1.0, 2, 0), (0.7, 9, 2**32 + 3)):
+        tok = fs.sample_fused(Hd, Wd, T, seed, step, variant="mfma", vocab_tile=tile, group_size=G).cpu().numpy()
+        check_grouped_parity(H, W, T, seed, step, G, np.arange(B), tok)

@@ -400,3 +400,25 @@ def test_full_size_sampled_rows(fs, full_workload):
             total += n
             near += k
     print(f"{wl.name}: {total} row checks over B={list(wl.batches)}, near-tie fraction {near / total:.4f}")
+
+
+@pytest.mark.parametrize("B", [65, 150, 300])
+def test_row_major_wide_kernel(fs, B):
+    """Row-major W with D a multiple of 256 above 64 rows: the wide kernel reads
+    the rows directly (vocab tile 256, 128-column batch tiles); sampling,
+    greedy, logits store and the unfused path; same tokens as the tiled layout."""
+    import torch
+    D, V = 512, 2053
+    H, W = _rand_head(B + 31, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    assert fs.num_vocab_tiles(B, D, V) == (V + 255) // 256
+    tw = fs.TiledWeights(Wd)
+    for T, seed, step in ((1.0, 0, 0), (0.6, 77, 2**32 + 1), (0.0, 0, 0)):
+        tok = fs.sample_fused(Hd, Wd, T, seed, step).cpu().numpy()
+        check_parity(H, W, T, seed, step, np.arange(B), tok)
+        assert np.array_equal(tok, fs.sample_fused(Hd, tw, T, seed, step).cpu().numpy())
+    l32 = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda")
+    fs.sample_fused(Hd, Wd, 1.0, 0, 0, logits=l32)
+    assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - oracle.exact_logits(H, W))) < 1e-4
+    tok = fs.sample_unfused(Hd, Wd, 1.0, 4, 4, logits_dtype=torch.float32).cpu().numpy()
+    check_parity(H, W, 1.0, 4, 4, np.arange(B), tok)
