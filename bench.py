@@ -175,9 +175,28 @@ def cpu_baseline(H, W, wl, B, budget_s=10.0):
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 10:
             break
+    # one step split into its two parts: the fp64 logits (BLAS) and the rest
+    # (Philox, Gumbel, perturbed argmax; numpy on one thread)
+    t1 = time.perf_counter()
+    oracle.exact_logits(H[:B], W)
+    gemm_s = time.perf_counter() - t1
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
     return {"value": B * steps / el, "unit": "samples/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} full decode step(s) of the workload (B={B} rows x V={wl.V}), "
-                      f"{el:.1f} s on the host, fp64 numpy/BLAS"}
+                      f"{el:.1f} s on the host, fp64 numpy/BLAS",
+            "seconds_per_step": el / steps, "logits_seconds_per_step": gemm_s,
+            "noise_and_argmax_seconds_per_step": max(el / steps - gemm_s, 0.0),
+            "cpu_model": cpu_model, "cpu_count": os.cpu_count(), "affinity_cores": affinity,
+            "blas_threads": int(threads)}
 
 
 def traffic_record(kernel: str, workload: str, B: int):
@@ -291,6 +310,10 @@ def main():
                                args.min_warmup_ms)
             rec["unfused_bf16_ms_per_step"] = u16
             rec["fused_speedup_vs_unfused_bf16"] = u16 / ms
+            u32 = time_unfused(fs, Hb, weights, wl, args.steps, args.warmup, b, torch.float32,
+                               args.min_warmup_ms)
+            rec["unfused_f32_ms_per_step"] = u32
+            rec["fused_speedup_vs_unfused_f32"] = u32 / ms
             # IO model (Section 3): with bf16 logits, the unfused path moves
             # 2*B*V*2 bytes more than the fused one (write + read back) and the
             # store-logits option B*V*2 more (write), on top of the V*D*2 of W.
@@ -299,7 +322,9 @@ def main():
                                "store_overhead": st / ms - 1.0,
                                "store_overhead_predicted": b / wl.D,
                                "unfused_overhead": u16 / ms - 1.0,
-                               "unfused_overhead_predicted": 2 * b / wl.D}
+                               "unfused_overhead_predicted": 2 * b / wl.D,
+                               "unfused_f32_overhead": u32 / ms - 1.0,
+                               "unfused_f32_overhead_predicted": 2 * b * 4 / (wl.D * esz)}
         log(f"[bench] B={b}: {ms * 1e3:.1f} us/step, stage1 {s1 * 1e3:.1f} us "
             f"({rec['stage1_GBps']:.0f} GB/s, {rec['stage1_TFLOPs']:.0f} TFLOP/s)" +
             (f", unfused {rec['unfused_bf16_ms_per_step'] * 1e3:.1f} us, store-logits overhead "
@@ -385,6 +410,9 @@ def main():
         result["unfused_bf16"] = {"ms_per_step": head["unfused_bf16_ms_per_step"],
                                   "samples_per_s": B / (head["unfused_bf16_ms_per_step"] * 1e-3),
                                   "fused_speedup": head["fused_speedup_vs_unfused_bf16"]}
+        result["unfused_f32"] = {"ms_per_step": head["unfused_f32_ms_per_step"],
+                                 "samples_per_s": B / (head["unfused_f32_ms_per_step"] * 1e-3),
+                                 "fused_speedup": head["fused_speedup_vs_unfused_f32"]}
         result["io_model"] = head["io_model"]
     if sweep:
         result["sweep"] = [head] + sweep
