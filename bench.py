@@ -5,11 +5,15 @@ synthetic hidden states against a resident LM head. Default workload: the
 Llama-3-8B-shaped head (D=4096, V=128256, bf16) at B=64, with W held in the
 tiled matrix-core layout (repacked once, before timing; --layout rows times
 the row-major path). Prints ONE JSON line with samples/s, the Stage-1
-kernel's achieved HBM bandwidth against MI355X's 8 TB/s, the unfused
-baseline and the row-major layout beside it, and the CPU oracle's rate.
+kernel's achieved HBM bandwidth against MI355X's 8 TB/s (and its counter-
+measured traffic when profiles/ holds a record for these sources), and
+beside them: single-pass, the grouped variant, the unfused baseline (bf16 and
+fp32 logits) with the IO model's prediction, the row-major layout, and the
+CPU oracle's rate. --sweep adds every B of the workload, each with its HBM
+and MFMA fractions.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--batch B] [--sweep]
-                  [--layout auto|tiled|rows] [--probe]
+                  [--layout auto|tiled|rows] [--group-size G] [--probe]
 """
 from __future__ import annotations
 
@@ -17,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,12 +44,24 @@ STAGE1_SOURCES = ("include/flashsample.h", "lm_head_gemm_amd/csrc/fs_common.h",
                   "lm_head_gemm_amd/csrc/stage1_tiled.hip", "lm_head_gemm_amd/csrc/api.hip")
 
 
-def source_hash() -> str:
-    """Hash of STAGE1_SOURCES: identifies the kernel a traffic record belongs to."""
+def code_of(text: str) -> str:
+    """C/C++ source without comments and blank space: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def source_hash(read=None) -> str:
+    """Hash of the code (comments and layout ignored) of STAGE1_SOURCES:
+    identifies the kernel a traffic record belongs to."""
     h = hashlib.sha256()
     for f in STAGE1_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        if read is None:
+            with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(f.encode() + code_of(text).encode())
     return h.hexdigest()[:16]
 
 

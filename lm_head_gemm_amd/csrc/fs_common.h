@@ -1,8 +1,11 @@
 // Internal header shared by the HIP translation units of libflashsample.
 //
-// Device side: the noise (Philox4x32-10 -> uniform -> Gumbel), the packed
-// 64-bit candidate key, and small wavefront helpers. Host side: the launch
-// helper and the declarations of each kernel family's launcher.
+// Device side: the noise (Philox4x32-10 -> uniform -> Gumbel, and the group
+// stream of the grouped variant), log-mass pairs, the packed 64-bit candidate
+// key and the running maximum, the logits store, candidate publication
+// (two-stage and single-pass), and small wavefront helpers. Host side: the
+// launch helper, the Stage-1 argument block and the declarations of each
+// kernel family's launcher.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,6 +1,9 @@
 // Stage 1, matrix-core regime: FlashSampling's fused kernel (arXiv
 // 2603.15854, Section 3, "Stage 1 (Fused Kernel)") on CDNA4 bf16 MFMA, for
 // batches large enough that the LM-head product is a real contraction.
+// Serves row-major W whose D is not a multiple of 256; for the others the
+// tiled-layout kernels read the rows directly (stage1_tiled.hip), which keeps
+// four times as many waves resident.
 //
 // Tile: one workgroup = BM vocab rows x BN batch rows; 4 waves, each owning
 // 16*MB consecutive vocab rows and all BN batch rows. The product is

@@ -27,8 +27,13 @@
 //    block per wave;
 //  * wide MFMA (B > 64): two row blocks per wave and 128-column batch tiles,
 //    H staged in sub-chunks and the B operands read one K step ahead.
+// The two MFMA kernels also serve row-major W whose D is a multiple of 256
+// (template flag ROWS): each lane then loads its A-operand piece from its
+// row instead of from the tiled copy.
 // All end in the same register epilogue: l * (1/T) + Gumbel(Philox word),
-// packed-key maximum per batch row, one candidate per (row, vocab tile).
+// a running maximum per batch row, one candidate key per (row, vocab tile);
+// optionally the tile's log-mass (grouped variant) and the logits (stored
+// through LDS as whole row segments).
 #include <type_traits>
 
 #include "fs_common.h"

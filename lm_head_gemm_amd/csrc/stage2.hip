@@ -1,6 +1,8 @@
 // Stage 2 of FlashSampling (arXiv 2603.15854, Section 3, "Stage 2
 // (Reduction)"): per batch row, the maximum of the packed candidate keys over
-// the vocab tiles, decoded to a token. Also the unfused baseline's sampler
+// the vocab tiles, decoded to a token; the grouped variant's Stage 2 (group
+// log-masses, the group draw, the chosen group's local sample). Also the
+// unfused baseline's sampler
 // (Gumbel-max over logits read back from device memory; the "sample from the
 // logits" step of the same section's IO model) and the noise test hooks.
 #include "fs_common.h"
