@@ -58,10 +58,14 @@ struct Plan {
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
 //   Row-major W: GEMV for fp32 inputs and bf16 batches up to kGemvMaxB rows
-//     (vocab tile: multiple of 16 rows), MFMA above (64 or 128 rows).
+//     (vocab tile: multiple of 16 rows), MFMA above (64 or 128 rows; with D a
+//     multiple of 256 the tiled-layout kernels read the rows directly and the
+//     256-row wide tile is the default from 65 rows on).
 //   Tiled W (bf16): the same split; vocab tile 64 or 128 rows (4 or 8 waves
 //     of one 16-row block each), and for MFMA batches from 65 rows on the
 //     256-row wide tile (8 waves of two blocks, batch tile 128).
+//   group_size > 0 (grouped variant): the MFMA kernels with the log-mass
+//     epilogue; groups must be unions of vocab tiles.
 bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* o, Plan* p,
                fs_status_t* why) {
   *why = FS_ERR_INVALID_ARGUMENT;
