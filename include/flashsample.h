@@ -36,6 +36,10 @@
  *  - Calls are asynchronous on `stream`: they validate, enqueue and return.
  *    Only the workspace and the outputs are written. Distinct calls may run
  *    concurrently if they use distinct workspaces and outputs.
+ *  - A call enqueues kernel launches only (plus the two timing event records
+ *    when fs_options asks for them): no allocation, copy or memset, so it can
+ *    be captured in a HIP graph and replayed; the kernel arguments (sizes,
+ *    temperature, seed, step, pointers) are fixed at capture.
  *  - Validation is synchronous; on any error nothing is enqueued.
  *  - No C++ exception crosses this interface.
  */

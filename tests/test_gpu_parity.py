@@ -422,3 +422,61 @@ def test_row_major_wide_kernel(fs, B):
     assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - oracle.exact_logits(H, W))) < 1e-4
     tok = fs.sample_unfused(Hd, Wd, 1.0, 4, 4, logits_dtype=torch.float32).cpu().numpy()
     check_parity(H, W, 1.0, 4, 4, np.arange(B), tok)
+
+
+def test_concurrent_streams_with_distinct_workspaces(fs):
+    """Calls on two streams with their own workspaces and outputs overlap
+    safely and give the sequential results (the header's concurrency rule)."""
+    import torch
+    B, D, V = 40, 512, 3001
+    H, W = _rand_head(41, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    tw = fs.TiledWeights(Wd)
+    want = [fs.sample_fused(Hd, tw, 1.0, 3, step).cpu().numpy() for step in range(8)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    ws = [torch.empty(fs.workspace_bytes(B, D, V, tiled=True), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    outs = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(8)]
+    torch.cuda.synchronize()
+    for step in range(8):
+        k = step % 2
+        with torch.cuda.stream(streams[k]):
+            fs.sample_fused(Hd, tw, 1.0, 3, step, out=outs[step], workspace=ws[k], stream=streams[k])
+    torch.cuda.synchronize()
+    for step in range(8):
+        assert np.array_equal(outs[step].cpu().numpy(), want[step])
+
+
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_graph_capture_and_replay(fs, single_pass):
+    """A fused call enqueues only kernel launches, so it can be captured in a
+    HIP graph: every replay (with new hidden states copied into the captured
+    input between replays, and eager calls in between) equals the eager call."""
+    import torch
+    B, D, V = 24, 1024, 2053
+    H, W = _rand_head(43, B, D, V)
+    Hd = to_device(H)
+    tw = fs.TiledWeights(to_device(W))
+    rng = np.random.default_rng(5)
+    ws = torch.empty(fs.workspace_bytes(B, D, V, tiled=True, single_pass=single_pass), dtype=torch.uint8, device="cuda")
+    fs.workspace_reset(ws)
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    static_h = Hd.clone()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):   # warm the call on the capture stream first
+        fs.sample_fused(static_h, tw, 0.9, 7, 11, out=out, workspace=ws, single_pass=single_pass, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fs.sample_fused(static_h, tw, 0.9, 7, 11, out=out, workspace=ws, single_pass=single_pass, stream=s)
+    torch.cuda.synchronize()
+    eager_ws = torch.empty_like(ws)
+    fs.workspace_reset(eager_ws)
+    for rep in range(4):
+        Hn = inputs.f32_to_bf16_bits(rng.standard_normal((B, D), dtype=np.float32))
+        static_h.copy_(to_device(Hn))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        eager = fs.sample_fused(static_h, tw, 0.9, 7, 11, workspace=eager_ws, single_pass=single_pass).cpu().numpy()
+        assert np.array_equal(got, eager), f"replay {rep}"
+        check_parity(Hn, W, 0.9, 7, 11, np.arange(B), got)
