@@ -175,7 +175,7 @@ def time_unfused(fs, Hb, Ws, wl, steps, warmup, B, logits_dtype, min_warm_ms=0.0
     return t0.elapsed_time(t1) / steps
 
 
-def cpu_baseline(H, W, wl, B, budget_s=10.0):
+def cpu_baseline(H, W, wl, B, budget_s=12.0):
     """Times the CPU oracle on whole decode steps of this workload (all B rows,
     full vocabulary) until about budget_s seconds of work are done."""
     import oracle
@@ -190,7 +190,7 @@ def cpu_baseline(H, W, wl, B, budget_s=10.0):
         oracle.sample(H[:B], W, wl.temperature, wl.seed, steps)
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 10:
+        if el >= budget_s or steps >= 30:
             break
     # one step split into its two parts: the fp64 logits (BLAS) and the rest
     # (Philox, Gumbel, perturbed argmax; numpy on one thread)
