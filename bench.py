@@ -237,7 +237,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="llama3_8b")
-    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--batch", type=int, default=0,
+                    help="batch rows per step (default: 64, or the largest of the workload's sweep below 64)")
     ap.add_argument("--sweep", action="store_true", help="also time every B of the workload's sweep")
     ap.add_argument("--batches", default="", help="comma-separated batch sizes to sweep instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -291,7 +292,7 @@ def main():
     if args.temperature is not None:
         import dataclasses
         wl = dataclasses.replace(wl, temperature=args.temperature)
-    B = args.batch
+    B = args.batch or max(b for b in wl.batches if b <= 64)
     log(f"[bench] generating {wl.name}: D={wl.D} V={wl.V} {wl.dtype}, B={B}")
     t = time.perf_counter()
     b_need = max([wl.b_max, B] + [int(x) for x in args.batches.split(",") if x])

@@ -26,7 +26,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRows = 4;   // vocab rows per group (one Philox call covers them)
-constexpr int kJB = 4;     // 16-byte chunks per lane loaded before use
+constexpr int kJB = 4;     // 16-byte chunks per lane loaded before use (rows longer than 64 chunks)
 
 template <bool BF16>
 __device__ __forceinline__ float dot_chunk(const uint4& w, const uint4& h, float acc) {
@@ -82,7 +82,10 @@ __device__ __forceinline__ float transpose_reduce(float (&v)[N], int lane) {
   return x;
 }
 
-template <int BB, bool BF16, bool SAMPLE, bool STORE>
+// JB: 16-byte chunks per lane loaded before use; 1 when a row is at most 64
+// chunks (the loop then runs once and a larger JB only costs registers:
+// fp32, 8 batch rows, D = 256 went from 1 to 2 waves per SIMD).
+template <int BB, int JB, bool BF16, bool SAMPLE, bool STORE>
 __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
   constexpr int N = kRows * BB;             // partial sums per lane per row group
   constexpr int S = 6 - Log2<N>::value;     // lane bits below the value index
@@ -139,10 +142,10 @@ __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
 
-    for (int j0 = 0; j0 < nj; j0 += kJB) {
-      uint4 w[kJB][kRows];
+    for (int j0 = 0; j0 < nj; j0 += JB) {
+      uint4 w[JB][kRows];
 #pragma unroll
-      for (int jj = 0; jj < kJB; ++jj) {
+      for (int jj = 0; jj < JB; ++jj) {
         const int c = lane + 64 * (j0 + jj);
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
         }
       }
 #pragma unroll
-      for (int jj = 0; jj < kJB; ++jj) {
+      for (int jj = 0; jj < JB; ++jj) {
         const int c = lane + 64 * (j0 + jj);
         if (c < nch) {
 #pragma unroll
@@ -207,16 +210,16 @@ __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
   }
 }
 
-template <int BB, bool BF16>
-hipError_t launch_bb(const Stage1Args& a, hipStream_t stream) {
+template <int BB, int JB, bool BF16>
+hipError_t launch_bb_jb(const Stage1Args& a, hipStream_t stream) {
   const bool sample = a.cand != nullptr;
   const bool store = a.logits != nullptr;
   const dim3 grid(a.n_tiles, (a.B + BB - 1) / BB);
   const size_t lds = (size_t)BB * a.D * (BF16 ? 2 : 4);
   void (*k)(Stage1Args) = nullptr;
-  if (sample && store) k = stage1_gemv_kernel<BB, BF16, true, true>;
-  else if (sample) k = stage1_gemv_kernel<BB, BF16, true, false>;
-  else k = stage1_gemv_kernel<BB, BF16, false, true>;
+  if (sample && store) k = stage1_gemv_kernel<BB, JB, BF16, true, true>;
+  else if (sample) k = stage1_gemv_kernel<BB, JB, BF16, true, false>;
+  else k = stage1_gemv_kernel<BB, JB, BF16, false, true>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -226,14 +229,24 @@ hipError_t launch_bb(const Stage1Args& a, hipStream_t stream) {
   return launch(k, grid, dim3(kThreads), lds, stream, b);
 }
 
+template <int BB, bool BF16>
+hipError_t launch_bb(const Stage1Args& a, hipStream_t stream) {
+  const int nch = a.D / (BF16 ? 8 : 4);
+  return nch <= 64 ? launch_bb_jb<BB, 1, BF16>(a, stream) : launch_bb_jb<BB, kJB, BF16>(a, stream);
+}
+
 }  // namespace
 
-// Batch rows per workgroup: the smallest power of two >= B, up to 8, while
-// the tile of H fits 64 KiB of LDS.
+// Batch rows per workgroup: the smallest power of two >= B, up to 8 (bf16)
+// or 4 (fp32; 2 when a row of H is at most 1 KiB), while the tile of H fits
+// 64 KiB of LDS. Larger fp32 tiles hold too many registers: measured on a
+// 4096 x 256 fp32 head, B = 64 took 133 us with 8 rows per workgroup, 35
+// with 4 and 28 with 2; on 32768 x 1024, 4 rows beat 2 by 16%.
 int gemv_batch_tile(int64_t B, int64_t D, fs_dtype_t dtype) {
   const int64_t esz = dtype == FS_DTYPE_BF16 ? 2 : 4;
+  const int cap = esz == 2 ? 8 : D * esz <= 1024 ? 2 : 4;
   int bb = 1;
-  while (bb < 8 && bb < B) bb *= 2;
+  while (bb < cap && bb < B) bb *= 2;
   while (bb > 1 && bb * D * esz > 65536) bb /= 2;
   return bb;
 }

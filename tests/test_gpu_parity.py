@@ -245,6 +245,19 @@ def test_single_pass_equals_two_stage(fs, layout, variant, dtype, B, D, V):
         check_parity(H, W, T, seed, step, np.arange(B), one)
 
 
+@pytest.mark.parametrize("B,D", [(2, 128), (5, 256), (64, 256), (9, 260), (64, 1032)])
+def test_f32_gemv_batch_tiles(fs, B, D):
+    """fp32 heads past a single row: 2-row batch tiles (H rows of at most
+    1 KiB) and 4-row ones, one and four 16-byte chunks per lane in flight,
+    ragged last batch tile."""
+    V = 1500
+    H, W = _rand_head(B + D, B, D, V, "f32")
+    Hd, Wd = to_device(H), to_device(W)
+    for T, seed, step in ((1.0, 3, 1), (0.0, 0, 0)):
+        tok = fs.sample_fused(Hd, Wd, T, seed, step).cpu().numpy()
+        check_parity(H, W, T, seed, step, np.arange(B), tok)
+
+
 def test_batch_prefix_and_repeat_determinism(fs):
     B, D, V = 13, 256, 3001
     H, W = _rand_head(9, B, D, V)
