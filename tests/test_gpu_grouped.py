@@ -32,7 +32,7 @@ def _rand_head(seed, B, D, V, sigma=0.05):
 
 @pytest.mark.parametrize("tile,G", [(64, 64), (64, 192), (128, 128), (128, 512), (256, 256), (256, 1024)])
 @pytest.mark.parametrize("B,D,V", [(1, 64, 1000), (5, 520, 2001), (33, 1032, 4099), (70, 264, 3000),
-                                   (150, 512, 2053)])
+                                   (150, 512, 2053), (300, 264, 1100)])
 def test_grouped_parity(fs, tile, G, B, D, V):
     H, W = _rand_head(B * 13 + D + V + G, B, D, V)
     Hd = to_device(H)
