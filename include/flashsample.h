@@ -64,7 +64,9 @@ typedef enum fs_status {
 
 typedef enum fs_dtype { FS_DTYPE_BF16 = 0, FS_DTYPE_F32 = 1 } fs_dtype_t;
 
-/* Stage-1 kernel family. AUTO picks by dtype and batch size. */
+/* Stage-1 kernel family. AUTO: GEMV (wavefront dot products) up to 2 batch
+ * rows, matrix cores above (bf16: v_mfma_f32_16x16x32_bf16; fp32, row-major
+ * W only: v_mfma_f32_16x16x4_f32, fp32 products and sums). */
 typedef enum fs_variant { FS_VARIANT_AUTO = 0, FS_VARIANT_GEMV = 1, FS_VARIANT_MFMA = 2 } fs_variant_t;
 
 /* Layout of the W argument.
@@ -83,7 +85,8 @@ typedef struct fs_options {
   int32_t vocab_tile;      /* rows per Stage-1 vocab tile; 0 = variant default.
                               Row-major W: a multiple of the variant's granule
                               (fs_vocab_tile_granule); MFMA: 64 or 128, or 256
-                              when D is a multiple of 256. Tiled W: 64 or 128,
+                              when D is a multiple of 256 (fp32: 128 only,
+                              the fp32 matrix-core kernel). Tiled W: 64 or 128,
                               or 256 for MFMA. 256 is the wide kernel (8 waves
                               of two 16-row blocks, 128-column batch tiles; the
                               default from B = 65 on where allowed). */

@@ -26,7 +26,7 @@ constexpr int32_t kTiledWideBatch = 128;    // batch tile of the wide kernel
 constexpr int64_t kTiledWideMinB = 65;      // batches from here on use the wide kernel
 constexpr int32_t kMfmaSmallBTile = 64;    // one 16-row block per wave
 constexpr int32_t kMfmaLargeBTile = 128;    // two blocks per wave above 32 rows
-constexpr int64_t kGemvMaxB = 2;            // bf16 batches above this use the MFMA kernel
+constexpr int64_t kGemvMaxB = 2;            // batches above this use the MFMA kernels
 constexpr int32_t kSamplePart = 2048;       // unfused sampler: vocab entries per workgroup
 constexpr size_t kAlign = 256;
 // The GEMV kernels stage whole H rows in LDS (160 KiB per workgroup) next to
@@ -59,10 +59,11 @@ struct Plan {
 };
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
-//   Row-major W: GEMV for fp32 inputs and bf16 batches up to kGemvMaxB rows
-//     (vocab tile: multiple of 16 rows), MFMA above (64 or 128 rows; with D a
-//     multiple of 256 the tiled-layout kernels read the rows directly and the
-//     256-row wide tile is the default from 65 rows on).
+//   Row-major W: GEMV for batches up to kGemvMaxB rows (vocab tile: multiple
+//     of 16 rows), MFMA above: bf16 64 or 128 rows (with D a multiple of 256
+//     the tiled-layout kernels read the rows directly and the 256-row wide
+//     tile is the default from 65 rows on); fp32 the fp32 matrix-core kernel
+//     (128 rows).
 //   Tiled W (bf16): the same split; vocab tile 64 or 128 rows (4 or 8 waves
 //     of one 16-row block each), and for MFMA batches from 65 rows on the
 //     256-row wide tile (8 waves of two blocks, batch tile 128).
@@ -88,11 +89,24 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
     }
     variant = FS_VARIANT_MFMA;
   }
-  if (variant == FS_VARIANT_AUTO)
-    variant = (dtype == FS_DTYPE_BF16 && B > kGemvMaxB) ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
   int32_t tile = o ? o->vocab_tile : 0;
   const int32_t bt = o ? o->batch_tile : 0;
   if (bt != 0 && bt != 16 && bt != 32 && bt != 64 && bt != kTiledWideBatch) return false;
+  if (variant == FS_VARIANT_AUTO)
+    variant = B > kGemvMaxB ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
+  if (variant == FS_VARIANT_MFMA && dtype == FS_DTYPE_F32 && layout == FS_LAYOUT_ROWS) {
+    // fp32 matrix-core kernel: 128-row vocab tiles, batch tiles of 16, 32 or 64
+    if (tile == 0) tile = mfma_f32_tile_rows();
+    if (tile != mfma_f32_tile_rows() || bt == kTiledWideBatch) return false;
+    p->variant = FS_VARIANT_MFMA;
+    p->tile = tile;
+    p->n_tiles = (V + tile - 1) / tile;
+    p->batch_tile = bt;
+    p->tiled = false;
+    p->single_pass = o && o->single_pass;
+    p->group_size = 0;
+    return true;
+  }
   if (layout == FS_LAYOUT_TILED) {
     if (dtype != FS_DTYPE_BF16) {
       *why = FS_ERR_UNSUPPORTED;
@@ -137,6 +151,7 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
 hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream) {
   if (p.tiled) return launch_stage1_tiled(a, p.variant == FS_VARIANT_MFMA, stream);
   if (p.variant != FS_VARIANT_MFMA) return launch_stage1_gemv(a, dtype, stream);
+  if (dtype == FS_DTYPE_F32) return launch_stage1_mfma_f32(a, stream);
   // row-major MFMA: the A operand straight from the rows when D is a multiple
   // of the K block, else the kernel that transposes W through LDS
   return rows_direct_ok(a.D) ? launch_stage1_rows_direct(a, stream) : launch_stage1_mfma(a, stream);

@@ -257,6 +257,28 @@ __device__ __forceinline__ void store_logits4(const Stage1Args& a, int b, int v0
   }
 }
 
+// Launch index -> (vocab tile, batch tile) for the matrix-core kernels: the
+// n_bt batch tiles of one vocab tile get consecutive slots on one XCD
+// (workgroup i runs on XCD i mod 8), so the tile of W comes from HBM once and
+// is re-read from that XCD's L2. Returns false for padding slots of a grid
+// rounded up to a multiple of kXcds.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool tile_of(int L, int n_vt, int n_bt, int* vt, int* bt) {
+  if (n_bt == 1) {
+    *vt = L;
+    *bt = 0;
+    return L < n_vt;
+  }
+  const int G = n_vt * n_bt;
+  const int per = (G + kXcds - 1) / kXcds;
+  const int logical = (L % kXcds) * per + L / kXcds;
+  if (logical >= G) return false;
+  *vt = logical / n_bt;
+  *bt = logical - *vt * n_bt;
+  return true;
+}
+
 // Publishes one workgroup's best key per batch row (k is meaningful for
 // tid < n_rows, rows b0 .. b0 + n_rows - 1; every thread of the workgroup
 // must call this).
@@ -306,6 +328,8 @@ hipError_t launch_stage1_mfma(const Stage1Args& a, hipStream_t stream);
 hipError_t launch_stage1_tiled(const Stage1Args& a, bool mfma, hipStream_t stream);
 bool rows_direct_ok(int64_t D);
 hipError_t launch_stage1_rows_direct(const Stage1Args& a, hipStream_t stream);
+hipError_t launch_stage1_mfma_f32(const Stage1Args& a, hipStream_t stream);
+int32_t mfma_f32_tile_rows();
 hipError_t launch_pack_tiled(const void* W, int64_t ldw, int32_t V, int32_t D, void* out, hipStream_t stream);
 int64_t tiled_weights_bytes(int64_t V, int64_t D);
 int mfma_tile_rows(int blocks_per_wave);

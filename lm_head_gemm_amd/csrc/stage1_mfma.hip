@@ -40,7 +40,6 @@ constexpr int kWaves = 4;
 constexpr int kKS = 8;               // MFMA K steps (of 32) per K chunk
 constexpr int kBK = 32 * kKS;        // 256
 constexpr int kLdsRow = kBK + 16;    // padded H row in LDS (elements): a stride of an odd multiple of 32 bytes reads conflict-free
-constexpr int kXcds = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -48,24 +47,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Maps the launch index to (vocab tile, batch tile) so that the n_bt batch
-// tiles of one vocab tile run back to back on one XCD (workgroup i goes to
-// XCD i mod 8). Returns false for the padding slots of the grid.
-__device__ __forceinline__ bool tile_of(int L, int n_vt, int n_bt, int* vt, int* bt) {
-  if (n_bt == 1) {
-    *vt = L;
-    *bt = 0;
-    return L < n_vt;
-  }
-  const int G = n_vt * n_bt;
-  const int per = (G + kXcds - 1) / kXcds;
-  const int logical = (L % kXcds) * per + L / kXcds;
-  if (logical >= G) return false;
-  *vt = logical / n_bt;
-  *bt = logical - *vt * n_bt;
-  return true;
 }
 
 template <int NB, int MB, bool SAMPLE, bool STORE>

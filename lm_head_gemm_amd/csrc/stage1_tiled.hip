@@ -49,7 +49,6 @@ constexpr int kBlock16 = kKS * 64;  // 16-byte pieces per block
 // operand reads (16 lanes of 16 rows per access); a 16-byte pad conflicts
 // 2-way on gfx950.
 constexpr int kLdsRow = kBK + 16;
-constexpr int kXcds = 8;
 constexpr int kGroup = 8;           // row blocks per group in the tiled layout
 constexpr int64_t kMaxHLds = 159 * 1024;  // LDS bytes for staged H rows (the rest: reduction arrays)
 
@@ -74,24 +73,6 @@ __device__ __forceinline__ float dot8_bf16(const uint4& w, const uint4& h, float
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, h.w), acc, false);
   return acc;
 }
-
-// Same mapping as the row-major MFMA kernel: batch tiles of one vocab tile
-// run back to back on one XCD (workgroup i goes to XCD i mod 8).
-__device__ __forceinline__ bool tile_of(int L, int n_vt, int n_bt, int* vt, int* bt) {
-  if (n_bt == 1) {
-    *vt = L;
-    *bt = 0;
-    return L < n_vt;
-  }
-  const int G = n_vt * n_bt;
-  const int per = (G + kXcds - 1) / kXcds;
-  const int logical = (L % kXcds) * per + L / kXcds;
-  if (logical >= G) return false;
-  *vt = logical / n_bt;
-  *bt = logical - *vt * n_bt;
-  return true;
-}
-
 
 // ---------------------------------------------------------------- pack
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W, int64_t ldw, int32_t V,

@@ -239,3 +239,29 @@ def test_grouped_option_validation(lib):
     base = [FAKE, 64, FAKE, 64, BF16, 2, 64, 1000, 1.0, 0, 0, F32, FAKE, 1 << 20, FAKE, None]
     o.weights_layout = 1
     assert lib.fs_sample_unfused_ex(*base, ctypes.byref(o)) == UNSUPPORTED
+
+
+def test_f32_matrix_core_options(lib):
+    """fp32 heads: GEMV up to 2 rows, the fp32 matrix-core kernel above
+    (row-major only, 128-row vocab tiles, batch tiles 16/32/64)."""
+    from lm_head_gemm_amd.flashsample import FsOptions
+    V = 1000
+    assert lib.fs_num_vocab_tiles(2, 256, V, F32, None) == math.ceil(V / 16)
+    assert lib.fs_num_vocab_tiles(3, 256, V, F32, None) == math.ceil(V / 128)
+    o = FsOptions()
+    o.variant = 2  # MFMA
+    assert lib.fs_num_vocab_tiles(1, 256, V, F32, ctypes.byref(o)) == math.ceil(V / 128)
+    o.vocab_tile = 64
+    assert lib.fs_num_vocab_tiles(1, 256, V, F32, ctypes.byref(o)) == -1
+    o.vocab_tile = 128
+    o.batch_tile = 32
+    assert lib.fs_num_vocab_tiles(40, 256, V, F32, ctypes.byref(o)) == math.ceil(V / 128)
+    o.batch_tile = 128
+    assert lib.fs_num_vocab_tiles(40, 256, V, F32, ctypes.byref(o)) == -1
+    o = FsOptions()
+    o.group_size = 1024
+    assert _fused(lib, opts=o, dtype=F32, B=16) == UNSUPPORTED
+    o = FsOptions()
+    o.weights_layout = 1
+    o.variant = 2
+    assert _fused(lib, opts=o, dtype=F32, B=16) == UNSUPPORTED

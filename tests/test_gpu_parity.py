@@ -220,7 +220,7 @@ def test_tiled_wide_store_and_unfused(fs, B):
 
 
 @pytest.mark.parametrize("layout,variant,dtype", [
-    ("rows", "gemv", "bf16"), ("rows", "mfma", "bf16"), ("rows", "gemv", "f32"),
+    ("rows", "gemv", "bf16"), ("rows", "mfma", "bf16"), ("rows", "gemv", "f32"), ("rows", "mfma", "f32"),
     ("tiled", "gemv", "bf16"), ("tiled", "mfma", "bf16"),
 ])
 @pytest.mark.parametrize("B,D,V", [(1, 256, 4099), (3, 520, 2001), (17, 1032, 3000), (64, 264, 1500),
@@ -245,17 +245,26 @@ def test_single_pass_equals_two_stage(fs, layout, variant, dtype, B, D, V):
         check_parity(H, W, T, seed, step, np.arange(B), one)
 
 
-@pytest.mark.parametrize("B,D", [(2, 128), (5, 256), (64, 256), (9, 260), (64, 1032)])
-def test_f32_gemv_batch_tiles(fs, B, D):
-    """fp32 heads past a single row: 2-row batch tiles (H rows of at most
-    1 KiB) and 4-row ones, one and four 16-byte chunks per lane in flight,
-    ragged last batch tile."""
+@pytest.mark.parametrize("B,D", [(2, 128), (5, 256), (64, 256), (9, 260), (64, 1032), (150, 132)])
+@pytest.mark.parametrize("variant", ["auto", "gemv", "mfma"])
+def test_f32_heads_past_one_row(fs, B, D, variant):
+    """fp32 heads: the GEMV kernel's 2- and 4-row batch tiles (one or four
+    16-byte chunks per lane in flight) and the fp32 matrix-core kernel
+    (v_mfma_f32_16x16x4_f32; ragged K block, ragged batch and vocab tiles),
+    sampling, greedy, the logits store and the unfused baseline."""
+    import torch
     V = 1500
     H, W = _rand_head(B + D, B, D, V, "f32")
     Hd, Wd = to_device(H), to_device(W)
     for T, seed, step in ((1.0, 3, 1), (0.0, 0, 0)):
-        tok = fs.sample_fused(Hd, Wd, T, seed, step).cpu().numpy()
+        tok = fs.sample_fused(Hd, Wd, T, seed, step, variant=variant).cpu().numpy()
         check_parity(H, W, T, seed, step, np.arange(B), tok)
+    exact = oracle.exact_logits(H, W)
+    l32 = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda")
+    fs.sample_fused(Hd, Wd, 1.0, 3, 1, variant=variant, logits=l32)
+    assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - exact)) < 1e-4
+    tok = fs.sample_unfused(Hd, Wd, 0.8, 6, 2, variant=variant, logits_dtype=torch.float32).cpu().numpy()
+    check_parity(H, W, 0.8, 6, 2, np.arange(B), tok)
 
 
 def test_batch_prefix_and_repeat_determinism(fs):
