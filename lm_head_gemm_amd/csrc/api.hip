@@ -210,6 +210,7 @@ Stage1Args stage1_args(const void* H, int64_t ldh, const void* W, int64_t ldw, i
   a.V = (int32_t)V;
   a.greedy = T == 0.f;
   a.inv_t = T == 0.f ? 0.f : 1.0f / T;
+  a.score_scale = T == 0.f ? 0.f : (float)(1.0 / ((double)T * 0.693147180559945309417));
   a.nk = noise_key(seed, step);
   a.vocab_tile = p.tile;
   a.n_tiles = (int32_t)p.n_tiles;
@@ -356,7 +357,7 @@ fs_status_t fs_sample_unfused_ex(const void* H, int64_t ldh, const void* W, int6
   hipError_t e = launch_stage1(p, a, dtype, stream);
   if (e != hipSuccess) return fail_hip(e);
   // step 2: sampler that reads them back
-  e = launch_sample_logits(ws, ld, a.logits_bf16, a.B, a.V, a.inv_t, a.greedy, a.nk, kSamplePart, n_parts,
+  e = launch_sample_logits(ws, ld, a.logits_bf16, a.B, a.V, a.score_scale, a.greedy, a.nk, kSamplePart, n_parts,
                            partial, stream);
   if (e != hipSuccess) return fail_hip(e);
   e = launch_stage2(partial, a.B, n_parts, out_tokens, stream);

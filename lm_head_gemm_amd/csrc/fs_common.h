@@ -58,30 +58,47 @@ __device__ __forceinline__ uint32_t pick_word(const uint4& w, int j) {
   return j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
 }
 
-// Standard Gumbel from a 32-bit word: u = (x + 1/2) 2^-32, g = -ln(-ln u).
-// Both logarithms use the hardware base-2 logarithm (v_log_f32) scaled by
-// ln 2. The inner one, e = -ln u, is taken two ways:
+// Standard Gumbel from a 32-bit word, u = (x + 1/2) 2^-32, g = -ln(-ln u),
+// in base-2 units. The kernels compare perturbed scores
+//     s2 = l * (1 / (T ln 2)) + g2,   g2 = -log2(e2),   e2 = -log2 u,
+// which is s = l / T + g divided by ln 2 plus the constant log2(ln 2)
+// (g = ln 2 * g2 - ln(ln 2)): a positive affine map of s, so neither the
+// maximiser nor the order of any two scores changes, and the two scalings by
+// ln 2 of the natural-log form drop out. Both logarithms are the hardware
+// base-2 logarithm (v_log_f32). The inner one is taken two ways:
 //  * u <= 1/2 (x < 2^31): directly, from u formed with one rounding;
 //  * u >  1/2: from c = 1 - u = (~x + 1/2) 2^-32, formed from the integer
-//    (the largest Gumbels live here, where u itself cannot resolve them),
-//    with Goldberg's log1p correction: for w = fl(1 - c), w - 1 is exact and
-//    ln(1 - c) = ln(w) * (-c) / (w - 1) to within a few ulps
-//    (D. Goldberg, "What every computer scientist should know about
-//    floating-point arithmetic", 1991, the log(1 + x) theorem); w == 1 only
-//    when c < 2^-25, where ln(1 - c) = -c to fp32 precision.
+//    (the largest Gumbels live here, where u itself cannot resolve them).
+//    With w = fl(1 - c), d = (1 - w) - c is exact (Sterbenz: 1 - w is c up
+//    to the rounding of w, at most 2^-25), so 1 - c = w + d and
+//    ln(1 - c) = ln w + ln(1 + d / w) = ln w + d (2 - w) + O(d (1 - w)^2),
+//    an error below 2^-26 (first-order log1p, d / w ~ d (2 - w) on
+//    [1/2, 1]). w == 1 (c < 2^-25) needs no special case: ln w = 0, d = -c.
 // Each uniform carries one fp32 rounding (relative 2^-24), which moves g by
 // about 1e-7; the bound checked against the fp64 definition is 1e-5.
-__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
-  constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kInvLn2 = 1.44269504088896340736f;
+constexpr float kLn2f = 0.693147180559945309f;
+constexpr float kNegLnLn2 = 0.366512920581664327f;   // -ln(ln 2)
+
+__device__ __forceinline__ float gumbel2_from_word(uint32_t x) {
   const bool low = x < 0x80000000u;
   const float u = fmaf((float)x, 0x1p-32f, 0x1p-33f);
   const float c = fmaf((float)(~x), 0x1p-32f, 0x1p-33f);
   const float w = 1.0f - c;
-  const float arg = low ? u : w;
-  const float scale = low ? 1.0f : c * __builtin_amdgcn_rcpf(1.0f - w);
-  float e = -kLn2 * __builtin_amdgcn_logf(arg) * scale;
-  if (!low && w == 1.0f) e = c;
-  return -kLn2 * __builtin_amdgcn_logf(e);
+  const float d = (1.0f - w) - c;
+  const float corr = low ? 0.0f : d * (2.0f - w);          // ln(1 - c) - ln w
+  const float e2 = fmaf(corr, -kInvLn2, -__builtin_amdgcn_logf(low ? u : w));
+  return -__builtin_amdgcn_logf(e2);
+}
+
+// The same Gumbel in natural units (group noise, the noise test entry).
+__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
+  return fmaf(kLn2f, gumbel2_from_word(x), kNegLnLn2);
+}
+
+// Perturbed score of logit l in base-2 units (scale = 1 / (T ln 2)).
+__device__ __forceinline__ float score2(float l, float scale, uint32_t word) {
+  return fmaf(l, scale, gumbel2_from_word(word));
 }
 
 // Group stream of the grouped variant: the same key, counter word 0 tagged so
@@ -208,6 +225,7 @@ struct Stage1Args {
   int64_t ldw;
   int32_t B, D, V;
   float inv_t;          // 1 / T (unused when greedy)
+  float score_scale;    // 1 / (T ln 2): token scores are compared in base-2 units (score2)
   int32_t greedy;       // T == 0
   NoiseKey nk;
   int32_t vocab_tile;   // rows per tile
@@ -338,7 +356,7 @@ hipError_t launch_stage2(const uint64_t* cand, int32_t B, int32_t n_tiles, int32
 hipError_t launch_stage2_grouped(const uint64_t* cand, const float* mass, int32_t B, int32_t n_tiles,
                                  int32_t tiles_per_group, NoiseKey nk, int32_t* out, hipStream_t stream);
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,
-                                int32_t V, float inv_t, int32_t greedy, NoiseKey nk,
+                                int32_t V, float score_scale, int32_t greedy, NoiseKey nk,
                                 int32_t part, int32_t n_parts, uint64_t* partial,
                                 hipStream_t stream);
 hipError_t launch_test_philox(NoiseKey nk, uint32_t b, int64_t v0, int64_t n, uint32_t* out,

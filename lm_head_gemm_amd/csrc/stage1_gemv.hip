@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
       float s = l;
       if (!a.greedy) {
         const uint4 words = philox_quad(a.nk, (uint32_t)(row0 >> 2), (uint32_t)my_batch);
-        s = fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, my_r)));
+        s = score2(l, a.score_scale, pick_word(words, my_r));
       }
       const uint64_t key = valid ? pack_key(s, (uint32_t)row) : 0ull;
       best = umax64(best, key);

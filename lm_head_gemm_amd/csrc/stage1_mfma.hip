@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 2) void stage1_mfma_kernel(Stage1Args a, 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float l = acc[mb][nb][j];
-          const float s = a.greedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, j)));
+          const float s = a.greedy ? l : score2(l, a.score_scale, pick_word(words, j));
           const bool valid = v0 + j < tile_end && b < a.B;
           best = umax64(best, valid ? pack_key(s, (uint32_t)(v0 + j)) : 0ull);
         }

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(64 * kNW) void mfma_f32_kernel(Stage1Args a, int32_
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float l = acc[nb][j];
-        const float s = a.greedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, j)));
+        const float s = a.greedy ? l : score2(l, a.score_scale, pick_word(words, j));
         if (v0 + j < a.V) runmax_take(best, s, v0 + j);
       }
       uint64_t key = runmax_key(best);

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_tiled_kernel(Stage1Args a) {
     float s = l;
     if (!a.greedy) {
       const uint4 words = philox_quad(a.nk, (uint32_t)(v >> 2), (uint32_t)batch);
-      s = fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, r & 3)));
+      s = score2(l, a.score_scale, pick_word(words, r & 3));
     }
     uint64_t best = valid ? pack_key(s, (uint32_t)v) : 0ull;
 #pragma unroll
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float l = acc[nb][j];
-          const float s = kGreedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, j)));
+          const float s = kGreedy ? l : score2(l, a.score_scale, pick_word(words, j));
           if (kFull || v0 + j < a.V) runmax_take(best, s, v0 + j);
         }
         uint64_t key = runmax_key(best);
@@ -648,7 +648,7 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float l = acc[j][nb][e];
-            const float sc = kGreedy ? l : fmaf(l, a.inv_t, gumbel_from_word(pick_word(words, e)));
+            const float sc = kGreedy ? l : score2(l, a.score_scale, pick_word(words, e));
             if (kFull || v0 + e < a.V) runmax_take(best, sc, v0 + e);
           }
         }

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(NT) void stage2_grouped_kernel(const uint64_t* __re
 // four), and writes its best key to partial[part, row].
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void sample_logits_kernel(
-    const void* __restrict__ logits, int64_t ld, int32_t V, float inv_t, int32_t greedy,
+    const void* __restrict__ logits, int64_t ld, int32_t V, float score_scale, int32_t greedy,
     NoiseKey nk, int32_t part, int32_t n_parts, uint64_t* __restrict__ partial) {
   __shared__ uint64_t red[kThreads / 64];
   const int row = blockIdx.y;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void sample_logits_kernel(
     if (!greedy) words = philox_quad(nk, (uint32_t)(v0 >> 2), (uint32_t)row);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float s = greedy ? l[j] : fmaf(l[j], inv_t, gumbel_from_word(pick_word(words, j)));
+      const float s = greedy ? l[j] : score2(l[j], score_scale, pick_word(words, j));
       if (v0 + j < v_end) best = umax64(best, pack_key(s, (uint32_t)(v0 + j)));
     }
   }
@@ -242,14 +242,14 @@ hipError_t launch_stage2_grouped(const uint64_t* cand, const float* mass, int32_
 }
 
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,
-                                int32_t V, float inv_t, int32_t greedy, NoiseKey nk,
+                                int32_t V, float score_scale, int32_t greedy, NoiseKey nk,
                                 int32_t part, int32_t n_parts, uint64_t* partial,
                                 hipStream_t stream) {
   const dim3 grid(n_parts, B);
   if (logits_bf16)
-    return launch(sample_logits_kernel<true>, grid, dim3(kThreads), 0, stream, logits, ld, V, inv_t,
+    return launch(sample_logits_kernel<true>, grid, dim3(kThreads), 0, stream, logits, ld, V, score_scale,
                   greedy, nk, part, n_parts, partial);
-  return launch(sample_logits_kernel<false>, grid, dim3(kThreads), 0, stream, logits, ld, V, inv_t,
+  return launch(sample_logits_kernel<false>, grid, dim3(kThreads), 0, stream, logits, ld, V, score_scale,
                 greedy, nk, part, n_parts, partial);
 }
 
