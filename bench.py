@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3   # dense fp32 matrix peak (fp32 heads run v_mfma_f32_16x16x4_f32)
 
 
 def log(*a):
@@ -91,6 +92,21 @@ def warm(fn, warmup, min_ms):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     return i
+
+
+def roofline(rec, mfma_peak, traffic):
+    """Roofline block for the Stage-1 kernel: HBM-bound while its arithmetic
+    intensity (2BVD flops over its algorithmic bytes) is below the ridge
+    peak flops / 8 TB/s, matrix-core bound above it."""
+    ai = rec["flops"] / rec["stage1_bytes"]
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    common = {"traffic": traffic, "kernel": "stage1 (fused GEMM + Gumbel-max epilogue)",
+              "stage1_us": rec["stage1_ms"] * 1e3, "flop_per_byte": ai, "ridge_flop_per_byte": ridge}
+    if ai <= ridge:
+        return {"bound": "hbm", "achieved": rec["stage1_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": rec["stage1_GBps"] / HBM_PEAK_GBS, **common}
+    return {"bound": "mfma", "achieved": rec["stage1_TFLOPs"], "peak": mfma_peak, "unit": "TFLOP/s",
+            "frac": rec["stage1_TFLOPs"] / mfma_peak, **common}
 
 
 def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, batch_tile=0,
@@ -175,6 +191,27 @@ def time_unfused(fs, Hb, Ws, wl, steps, warmup, B, logits_dtype, min_warm_ms=0.0
     return t0.elapsed_time(t1) / steps
 
 
+def time_vendor_gemm(Hb, Wr, steps, warmup):
+    """ms per torch.matmul (hipBLASLt) H @ W^T into a bf16 logits buffer,
+    alternating the W copies: the library GEMM alone, with no noise and no
+    argmax. Context for the contraction's speed, not a sampler baseline."""
+    import torch
+    B, V = Hb.shape[0], Wr[0].shape[0]
+    outs = [torch.empty(B, V, dtype=torch.bfloat16, device="cuda") for _ in Wr]
+    for i in range(max(warmup, 10)):
+        torch.matmul(Hb, Wr[i % len(Wr)].t(), out=outs[i % len(Wr)])
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        torch.matmul(Hb, Wr[i % len(Wr)].t(), out=outs[i % len(Wr)])
+    t1.record()
+    torch.cuda.synchronize()
+    del outs
+    return t0.elapsed_time(t1) / steps
+
+
 def cpu_baseline(H, W, wl, B, budget_s=12.0):
     """Times the CPU oracle on whole decode steps of this workload (all B rows,
     full vocabulary) until about budget_s seconds of work are done."""
@@ -256,6 +293,8 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="also stream W once per step with the read probe (attainable bandwidth)")
     ap.add_argument("--no-rows", action="store_true", help="skip timing the row-major layout beside")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip timing the library GEMM (torch.matmul, logits only) beside, for context")
     ap.add_argument("--group-size", type=int, default=16384,
                     help="also time the grouped variant with groups of this many vocab entries (0: skip)")
     ap.add_argument("--single-pass", action="store_true",
@@ -304,10 +343,12 @@ def main():
     # step's tail of W from the 256 MB last-level cache
     Ws = [upload(W), upload(W)]
     esz = 2 if wl.dtype == "bf16" else 4
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
 
     single = args.single_pass
 
     def run(b, weights=None, single_pass=None):
+        main_weights = weights is None
         weights = Ws if weights is None else weights
         single_pass = single if single_pass is None else single_pass
         Hb = Hd[:b]
@@ -321,7 +362,7 @@ def main():
                "stage1_GBps": byts / (s1 * 1e-3) / 1e9, "stage1_bytes": byts, "n_tiles": nt,
                "hbm_frac": byts / (s1 * 1e-3) / 1e9 / HBM_PEAK_GBS,
                "flops": flops, "stage1_TFLOPs": flops / (s1 * 1e-3) / 1e12,
-               "mfma_frac": flops / (s1 * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+               "mfma_frac": flops / (s1 * 1e-3) / 1e12 / mfma_peak,
                "warmup_steps_run": n_warm}
         if not args.no_unfused:
             u16 = time_unfused(fs, Hb, weights, wl, args.steps, args.warmup, b, torch.bfloat16,
@@ -343,6 +384,10 @@ def main():
                                "unfused_overhead_predicted": 2 * b / wl.D,
                                "unfused_f32_overhead": u32 / ms - 1.0,
                                "unfused_f32_overhead_predicted": 2 * b * 4 / (wl.D * esz)}
+        if main_weights and vendor_rows is not None and wl.dtype == "bf16":
+            vg = time_vendor_gemm(Hb, vendor_rows, args.steps, args.warmup)
+            rec["vendor_gemm_logits_only_ms"] = vg
+            rec["fused_vs_vendor_gemm_only"] = vg / ms
         log(f"[bench] B={b}: {ms * 1e3:.1f} us/step, stage1 {s1 * 1e3:.1f} us "
             f"({rec['stage1_GBps']:.0f} GB/s, {rec['stage1_TFLOPs']:.0f} TFLOP/s)" +
             (f", unfused {rec['unfused_bf16_ms_per_step'] * 1e3:.1f} us, store-logits overhead "
@@ -351,13 +396,15 @@ def main():
         return rec
 
     Ws_rows = Ws
+    vendor_rows = None if args.no_vendor else Ws_rows
     if args.layout == "tiled":
         Ws = [fs.TiledWeights(w) for w in Ws_rows]
         torch.cuda.synchronize()
         if args.no_rows:
             del Ws_rows
             Ws_rows = None
-            torch.cuda.empty_cache()
+            if vendor_rows is None:
+                torch.cuda.empty_cache()
 
     head = run(B)
     sweep_bs = [int(x) for x in args.batches.split(",") if x] or (list(wl.batches) if args.sweep else [])
@@ -381,11 +428,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "D": wl.D, "V": wl.V, "temperature": wl.temperature,
                    "weights_layout": args.layout, "stage2": "folded into stage 1" if single else "separate kernel",
                    "vocab_tiles": head["n_tiles"], "W_copies_alternated": 2},
-        "roofline": {"bound": "hbm", "achieved": head["stage1_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["stage1_GBps"] / HBM_PEAK_GBS,
-                     "traffic": traffic_record("stage1", wl.name, B),
-                     "kernel": "stage1 (fused GEMM + Gumbel-max epilogue)",
-                     "stage1_us": head["stage1_ms"] * 1e3},
+        "roofline": roofline(head, mfma_peak, traffic_record("stage1", wl.name, B)),
     }
     other = run(B, single_pass=not single)
     result["single_pass" if not single else "two_stage"] = {
@@ -424,6 +467,11 @@ def main():
         pms = t0.elapsed_time(t1) / args.steps
         nbytes = flat.numel() * flat.element_size()
         result["read_probe"] = {"bytes": nbytes, "us": pms * 1e3, "GBps": nbytes / (pms * 1e-3) / 1e9}
+    if "vendor_gemm_logits_only_ms" in head:
+        result["vendor_gemm_context"] = {
+            "what": "torch.matmul (hipBLASLt) H @ W^T -> bf16 logits only: no noise, no argmax, not a sampler",
+            "ms": head["vendor_gemm_logits_only_ms"],
+            "fused_call_speedup_over_it": head["fused_vs_vendor_gemm_only"]}
     if "unfused_bf16_ms_per_step" in head:
         result["unfused_bf16"] = {"ms_per_step": head["unfused_bf16_ms_per_step"],
                                   "samples_per_s": B / (head["unfused_bf16_ms_per_step"] * 1e-3),
