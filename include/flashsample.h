@@ -40,7 +40,11 @@
  *    when fs_options asks for them): no allocation, copy or memset, so it can
  *    be captured in a HIP graph and replayed; the kernel arguments (sizes,
  *    temperature, seed, step, pointers) are fixed at capture.
- *  - Validation is synchronous; on any error nothing is enqueued.
+ *  - Validation is synchronous; on any error nothing is enqueued. A shape
+ *    whose first launch would count more work-items in one grid dimension
+ *    than a dispatch holds (2^32) is refused at that launch with FS_ERR_HIP
+ *    and fs_last_hip_error() == hipErrorInvalidConfiguration, still before
+ *    anything is enqueued.
  *  - No C++ exception crosses this interface.
  */
 #ifndef FLASHSAMPLE_H

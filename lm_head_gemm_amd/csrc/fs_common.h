@@ -205,9 +205,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // ------------------------------------------------------------------ host
 // Launch through hipLaunchKernel so the launch status comes back directly.
+// A dispatch counts work-items in 32 bits per dimension: blocks x threads
+// must stay below 2^32 (grids are sized in 64 bits and checked here before
+// they are narrowed to dim3).
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks > 0 && threads > 0 && blocks <= 0xFFFFFFFFll / threads;
+}
+
 template <typename... KArgs, typename... Args>
 inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
                          hipStream_t stream, Args&&... args) {
+  if (!grid_fits(grid.x, block.x) || !grid_fits(grid.y, block.y) || !grid_fits(grid.z, block.z))
+    return hipErrorInvalidConfiguration;
   std::tuple<KArgs...> packed(std::forward<Args>(args)...);
   return std::apply(
       [&](auto&... a) {

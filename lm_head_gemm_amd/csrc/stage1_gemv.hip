@@ -225,6 +225,7 @@ hipError_t launch_bb_jb(const Stage1Args& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   Stage1Args b = a;
+  if ((int64_t)grid.x * grid.y > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // workgroup count is int32
   b.total_wgs = (int32_t)(grid.x * grid.y);
   return launch(k, grid, dim3(kThreads), lds, stream, b);
 }

@@ -174,6 +174,7 @@ hipError_t launch_nb(const Stage1Args& a, hipStream_t stream) {
   const int n_bt = (a.B + BN - 1) / BN;
   const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
   void (*k)(Stage1Args, int32_t) = nullptr;
   if (sample && store) k = mfma_f32_kernel<NB, true, true>;
   else if (sample) k = mfma_f32_kernel<NB, true, false>;

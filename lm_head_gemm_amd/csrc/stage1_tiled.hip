@@ -706,6 +706,7 @@ hipError_t launch_gemv_bb(const Stage1Args& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   Stage1Args b = a;
+  if ((int64_t)grid.x * grid.y > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // workgroup count is int32
   b.total_wgs = (int32_t)(grid.x * grid.y);
   return launch(k, grid, dim3(64 * NW), lds, stream, b);
 }
@@ -727,6 +728,7 @@ hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   const int n_bt = (a.B + BN - 1) / BN;
   const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
   void (*k)(Stage1Args, int32_t) = nullptr;
   if (a.mass)
     k = store ? mfma_tiled_kernel<NB, NW, true, true, true, ROWS> : mfma_tiled_kernel<NB, NW, true, false, true, ROWS>;
@@ -744,6 +746,7 @@ hipError_t launch_mfma_wide_k(const Stage1Args& a, int n_bt, hipStream_t stream)
   const bool store = a.logits != nullptr;
   const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
   void (*k)(Stage1Args, int32_t) = nullptr;
   if (a.mass)
     k = store ? mfma_wide_kernel<true, true, true, ROWS, STREAMW> : mfma_wide_kernel<true, false, true, ROWS, STREAMW>;
@@ -783,6 +786,7 @@ int64_t tiled_weights_bytes(int64_t V, int64_t D) {
 hipError_t launch_pack_tiled(const void* W, int64_t ldw, int32_t V, int32_t D, void* out, hipStream_t stream) {
   const int nC = (D + kBK - 1) / kBK;
   const int64_t n16 = tiled_weights_bytes(V, D) / 16;
+  if ((n16 + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((n16 + 255) / 256));
   return launch(pack_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(W), ldw, V, D, nC, n16,
                 static_cast<uint4*>(out));

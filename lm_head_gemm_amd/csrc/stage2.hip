@@ -224,6 +224,7 @@ hipError_t launch_probe_read(const void* src, int64_t bytes, int64_t chunk_bytes
                              hipStream_t stream) {
   const int64_t n16 = bytes / 16;
   const int64_t chunk16 = chunk_bytes / 16;
+  if ((n16 + chunk16 - 1) / chunk16 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((n16 + chunk16 - 1) / chunk16));
   return launch(probe_read_kernel<8>, grid, dim3(kThreads), 0, stream, static_cast<const uint4*>(src), n16,
                 chunk16, sink);
@@ -255,11 +256,13 @@ hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_b
 
 hipError_t launch_test_philox(NoiseKey nk, uint32_t b, int64_t v0, int64_t n, uint32_t* out,
                               hipStream_t stream) {
+  if ((n + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
   return launch(test_philox_kernel, grid, dim3(kThreads), 0, stream, nk, b, v0, n, out);
 }
 
 hipError_t launch_test_gumbel(const uint32_t* words, int64_t n, float* out, hipStream_t stream) {
+  if ((n + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
   return launch(test_gumbel_kernel, grid, dim3(kThreads), 0, stream, words, n, out);
 }

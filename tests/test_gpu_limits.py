@@ -85,3 +85,21 @@ def test_two_million_vocab_rows(fs):
             tok = fs.sample_fused(Hd[:B], Wx, 1.0, 3, 4).cpu().numpy()
             sub = oracle.SampleResult(ref.idx[:B], ref.best[:B], ref.second[:B], ref.second_idx[:B])
             check_parity(H, W, 1.0, 3, 4, np.arange(B), tok, ref=sub)
+
+
+def test_launch_beyond_dispatch_limit_is_refused(fs):
+    """65536 rows over an 8M-row vocabulary need more work-items in one launch
+    dimension than a dispatch can count (2^32): the call fails with FS_ERR_HIP
+    (hipErrorInvalidConfiguration) before anything is enqueued, and the output
+    is left untouched. (Single-pass, so the workspace stays small.)"""
+    import torch
+    B, D, V = 65536, 8, 8 << 20
+    H = torch.zeros(B, D, dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros(V, D, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    with pytest.raises(fs.FlashSampleError) as err:
+        fs.sample_fused(H, W, 1.0, 0, 0, out=out, single_pass=True)
+    assert err.value.status == fs.FS_ERR_HIP
+    assert fs._lib.fs_last_hip_error() == 9   # hipErrorInvalidConfiguration
+    torch.cuda.synchronize()
+    assert int((out != -7).sum()) == 0
