@@ -191,6 +191,42 @@ def time_unfused(fs, Hb, Ws, wl, steps, warmup, B, logits_dtype, min_warm_ms=0.0
     return t0.elapsed_time(t1) / steps
 
 
+def time_graph(fs, Hb, Ws, wl, steps, B, reps=20):
+    """Decode steps 0 .. n-1 (n = min(steps, 64), each with its own step value,
+    so its own noise) captured once in a HIP graph and replayed: ms per step
+    with no host launch cost. The replayed tokens of the first and last step
+    are checked against eager calls."""
+    import torch
+    n = min(steps, 64)
+    tiled = isinstance(Ws[0], fs.TiledWeights)
+    ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, tiled=tiled), dtype=torch.uint8, device="cuda")
+    outs = torch.empty((n, B), dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    calls = lambda: [fs.sample_fused(Hb, Ws[i % len(Ws)], wl.temperature, wl.seed, i, out=outs[i],
+                                     workspace=ws, stream=s) for i in range(n)]
+    with torch.cuda.stream(s):
+        calls()                          # warm the calls on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / (reps * n)
+    for i in (0, n - 1):
+        eager = fs.sample_fused(Hb, Ws[i % len(Ws)], wl.temperature, wl.seed, i)
+        assert torch.equal(eager, outs[i]), f"graph replay differs from the eager call at step {i}"
+    return ms, n
+
+
 def time_vendor_gemm(Hb, Wr, steps, warmup):
     """ms per torch.matmul (hipBLASLt) H @ W^T into a bf16 logits buffer,
     alternating the W copies: the library GEMM alone, with no noise and no
@@ -293,6 +329,8 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="also stream W once per step with the read probe (attainable bandwidth)")
     ap.add_argument("--no-rows", action="store_true", help="skip timing the row-major layout beside")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the decode steps captured in one HIP graph and replayed (no host launch cost)")
     ap.add_argument("--no-vendor", action="store_true",
                     help="skip timing the library GEMM (torch.matmul, logits only) beside, for context")
     ap.add_argument("--group-size", type=int, default=16384,
@@ -467,6 +505,11 @@ def main():
         pms = t0.elapsed_time(t1) / args.steps
         nbytes = flat.numel() * flat.element_size()
         result["read_probe"] = {"bytes": nbytes, "us": pms * 1e3, "GBps": nbytes / (pms * 1e-3) / 1e9}
+    if args.graph:
+        gms, gn = time_graph(fs, Hd[:B], Ws, wl, args.steps, B)
+        result["graph_replay"] = {"steps_per_graph": gn, "ms_per_step": gms, "samples_per_s": B / (gms * 1e-3),
+                                  "speedup_over_launched": head["ms_per_step"] / gms}
+        log(f"[bench] graph replay: {gms * 1e3:.1f} us/step over {gn} captured steps")
     if "vendor_gemm_logits_only_ms" in head:
         result["vendor_gemm_context"] = {
             "what": "torch.matmul (hipBLASLt) H @ W^T -> bf16 logits only: no noise, no argmax, not a sampler",
