@@ -13,7 +13,7 @@ CPU oracle's rate. --sweep adds every B of the workload, each with its HBM
 and MFMA fractions.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--batch B] [--sweep]
-                  [--layout auto|tiled|rows] [--group-size G] [--probe]
+                  [--layout auto|tiled|rows] [--group-size G] [--probe] [--graph]
 """
 from __future__ import annotations
 
