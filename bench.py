@@ -110,13 +110,15 @@ def roofline(rec, mfma_peak, traffic):
 
 
 def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, batch_tile=0,
-               single_pass=False, min_warm_ms=0.0, group_size=0):
-    """Returns (ms per step, mean Stage-1 ms, warm-up steps run).
+               single_pass=False, min_warm_ms=0.0, group_size=0, repeats=1, runs_out=None):
+    """Returns (ms per step, median Stage-1 ms, warm-up steps run).
 
     The step time comes from `steps` back-to-back calls bracketed by two
-    events; the Stage-1 time from a second pass of `steps` calls in which the
-    library records an event pair around each Stage-1 launch on the same
-    stream (those extra records are kept out of the step time)."""
+    events (with repeats > 1: the median of that many such runs, whose
+    per-step times are appended to runs_out); the Stage-1 time from a second
+    pass of `steps` calls in which the library records an event pair around
+    each Stage-1 launch on the same stream (those extra records are kept out
+    of the step time)."""
     import torch
     T, seed = wl.temperature, wl.seed
     tiled = isinstance(Ws[0], fs.TiledWeights)
@@ -131,13 +133,18 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
     n_warm = warm(lambda i: fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw), warmup, min_warm_ms)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw)
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
+    runs = []
+    for _ in range(max(1, repeats)):
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw)
+        t1.record()
+        torch.cuda.synchronize()
+        runs.append(t0.elapsed_time(t1) / steps)
+    if runs_out is not None:
+        runs_out.extend(runs)
+    total_ms = float(np.median(runs)) * steps
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in ev:  # create the HIP events; the library re-records them around Stage 1
@@ -147,7 +154,7 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
     for i in range(steps):
         fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, events=ev[i], **kw)
     torch.cuda.synchronize()
-    s1 = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    s1 = float(np.median([a.elapsed_time(b) for a, b in ev]))   # robust to a stray slow record
     return total_ms / steps, s1, n_warm
 
 
@@ -309,6 +316,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed runs of --steps calls for the headline; value is from the median run")
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--batch", type=int, default=0,
                     help="batch rows per step (default: 64, or the largest of the workload's sweep below 64)")
@@ -390,8 +399,10 @@ def main():
         weights = Ws if weights is None else weights
         single_pass = single if single_pass is None else single_pass
         Hb = Hd[:b]
+        runs = []
         ms, s1, n_warm = time_fused(fs, Hb, weights, wl, args.steps, args.warmup, b, args.variant,
-                                    args.vocab_tile, args.batch_tile, single_pass, args.min_warmup_ms)
+                                    args.vocab_tile, args.batch_tile, single_pass, args.min_warmup_ms,
+                                    repeats=args.repeats, runs_out=runs)
         tiled = isinstance(weights[0], fs.TiledWeights)
         nt = fs.num_vocab_tiles(b, wl.D, wl.V, Hb.dtype, args.variant, args.vocab_tile, tiled=tiled)
         byts = stage1_bytes(b, wl.D, wl.V, esz, nt)
@@ -401,7 +412,7 @@ def main():
                "hbm_frac": byts / (s1 * 1e-3) / 1e9 / HBM_PEAK_GBS,
                "flops": flops, "stage1_TFLOPs": flops / (s1 * 1e-3) / 1e12,
                "mfma_frac": flops / (s1 * 1e-3) / 1e12 / mfma_peak,
-               "warmup_steps_run": n_warm}
+               "warmup_steps_run": n_warm, "ms_per_step_runs": runs, "ms_per_step_min": min(runs)}
         if not args.no_unfused:
             u16 = time_unfused(fs, Hb, weights, wl, args.steps, args.warmup, b, torch.bfloat16,
                                args.min_warmup_ms)
@@ -458,6 +469,9 @@ def main():
         "warmup": args.warmup,
         "warmup_steps_run": head["warmup_steps_run"],
         "ms_per_step": head["ms_per_step"],
+        "repeats": args.repeats,
+        "ms_per_step_runs": head["ms_per_step_runs"],
+        "ms_per_step_min": head["ms_per_step_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
