@@ -115,15 +115,17 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
 
     The step time comes from `steps` back-to-back calls bracketed by two
     events (with repeats > 1: the median of that many such runs, whose
-    per-step times are appended to runs_out); the Stage-1 time from a second
-    pass of `steps` calls in which the library records an event pair around
-    each Stage-1 launch on the same stream (those extra records are kept out
-    of the step time)."""
+    per-step times are appended to runs_out); the Stage-1 time from passes
+    of `steps` calls in which the library records an event pair around each
+    Stage-1 launch on the same stream (those extra records are kept out of
+    the step time). Timed runs and Stage-1 passes alternate, so both see the
+    same clocks while the part heats up under a long matrix-core load."""
     import torch
     T, seed = wl.temperature, wl.seed
     tiled = isinstance(Ws[0], fs.TiledWeights)
     ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, variant=variant, vocab_tile=vocab_tile,
-                                        tiled=tiled, single_pass=single_pass, group_size=group_size),
+                                        tiled=tiled, single_pass=single_pass, group_size=group_size,
+                                        batch_tile=batch_tile),
                      dtype=torch.uint8, device="cuda")
     if single_pass:
         fs.workspace_reset(ws)
@@ -133,7 +135,11 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
     n_warm = warm(lambda i: fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw), warmup, min_warm_ms)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    runs = []
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:  # create the HIP events; the library re-records them around Stage 1
+        a.record()
+        b.record()
+    runs, s1s = [], []
     for _ in range(max(1, repeats)):
         torch.cuda.synchronize()
         t0.record()
@@ -142,20 +148,14 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
         t1.record()
         torch.cuda.synchronize()
         runs.append(t0.elapsed_time(t1) / steps)
+        for i in range(steps):
+            fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, events=ev[i], **kw)
+        torch.cuda.synchronize()
+        s1s.extend(a.elapsed_time(b) for a, b in ev)
     if runs_out is not None:
         runs_out.extend(runs)
-    total_ms = float(np.median(runs)) * steps
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:  # create the HIP events; the library re-records them around Stage 1
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    for i in range(steps):
-        fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, events=ev[i], **kw)
-    torch.cuda.synchronize()
-    s1 = float(np.median([a.elapsed_time(b) for a, b in ev]))   # robust to a stray slow record
-    return total_ms / steps, s1, n_warm
+    s1 = float(np.median(s1s))   # robust to a stray slow record
+    return float(np.median(runs)), s1, n_warm
 
 
 def time_fused_store(fs, Hb, Ws, wl, steps, warmup, B, min_warm_ms=0.0):

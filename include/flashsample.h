@@ -101,7 +101,12 @@ typedef struct fs_options {
   int32_t batch_tile;      /* MFMA only: batch rows per workgroup (16, 32 or
                               64; 128 with the 256-row tiled tile, and only
                               there); 0 = chosen from B. Larger batches are
-                              split into tiles that re-read W from L2. */
+                              split into tiles that re-read W from L2.
+                              256: the 256 x 256 tile with both operands
+                              copied straight into LDS (tiled bf16 W, D a
+                              multiple of 32, fused sampling without stored
+                              logits or groups; else FS_ERR_UNSUPPORTED);
+                              never chosen by itself. */
   hipEvent_t stage1_start; /* non-null: recorded on `stream` right before and */
   hipEvent_t stage1_stop;  /* right after the Stage-1 launch (for timing) */
   int32_t weights_layout;  /* fs_layout_t of W */

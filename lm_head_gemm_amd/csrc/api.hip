@@ -23,6 +23,7 @@ constexpr int32_t kTiledGemvTile = 128;    // tiled layout: 8 waves x 16 rows
 constexpr int32_t kTiledMfmaTile = 128;     // tiled layout: 8 waves x 16 rows
 constexpr int32_t kTiledWideTile = 256;     // tiled layout: 8 waves x 2 x 16 rows
 constexpr int32_t kTiledWideBatch = 128;    // batch tile of the wide kernel
+constexpr int32_t kTiledBigBatch = 256;     // opt-in 256 x 256 tile (tiled, sampling only)
 constexpr int64_t kTiledWideMinB = 65;      // batches from here on use the wide kernel
 constexpr int32_t kMfmaSmallBTile = 64;    // one 16-row block per wave
 constexpr int32_t kMfmaLargeBTile = 128;    // two blocks per wave above 32 rows
@@ -91,7 +92,24 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   }
   int32_t tile = o ? o->vocab_tile : 0;
   const int32_t bt = o ? o->batch_tile : 0;
-  if (bt != 0 && bt != 16 && bt != 32 && bt != 64 && bt != kTiledWideBatch) return false;
+  if (bt != 0 && bt != 16 && bt != 32 && bt != 64 && bt != kTiledWideBatch && bt != kTiledBigBatch) return false;
+  if (bt == kTiledBigBatch) {
+    // the 256 x 256 tile: tiled bf16 W, D a multiple of 32, plain sampling
+    const bool ok = layout == FS_LAYOUT_TILED && dtype == FS_DTYPE_BF16 && D % 32 == 0 && group_size == 0 &&
+                    !(o && o->logits) && variant != FS_VARIANT_GEMV && (o->vocab_tile == 0 || o->vocab_tile == kTiledWideTile);
+    if (!ok) {
+      *why = FS_ERR_UNSUPPORTED;
+      return false;
+    }
+    p->variant = FS_VARIANT_MFMA;
+    p->tile = kTiledWideTile;
+    p->n_tiles = (V + kTiledWideTile - 1) / kTiledWideTile;
+    p->batch_tile = kTiledBigBatch;
+    p->tiled = true;
+    p->single_pass = o->single_pass;
+    p->group_size = 0;
+    return true;
+  }
   if (variant == FS_VARIANT_AUTO)
     variant = B > kGemvMaxB ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
   if (variant == FS_VARIANT_MFMA && dtype == FS_DTYPE_F32 && layout == FS_LAYOUT_ROWS) {
@@ -338,6 +356,7 @@ fs_status_t fs_sample_unfused_ex(const void* H, int64_t ldh, const void* W, int6
   if (st != FS_OK) return st;
   if (!dtype_ok(logits_dtype)) return FS_ERR_UNSUPPORTED;
   if (opts && opts->group_size != 0) return FS_ERR_UNSUPPORTED;   // the baseline is plain sampling
+  if (opts && opts->batch_tile == kTiledBigBatch) return FS_ERR_UNSUPPORTED;   // that tile only samples
   Plan p;
   if (!make_plan(B, D, V, dtype, opts, &p, &st)) return st;
   if (workspace_bytes < unfused_ws_bytes(B, V, logits_dtype)) return FS_ERR_WORKSPACE_TOO_SMALL;

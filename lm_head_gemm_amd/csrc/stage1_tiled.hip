@@ -691,6 +691,193 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
   }
 }
 
+// ------------------------------------------------------- MFMA, 256 x 256 tiles
+// Opt-in (batch_tile = 256; measured within 1-3% of the wide kernel at
+// B = 512 .. 1024, not ahead of it, so the plan does not pick it by itself).
+// Large batches on the tiled layout (D a multiple of 32): a workgroup of 8
+// waves owns a 256-row vocab tile and a 256-column batch tile; wave w
+// computes vocab quarter w & 3 (4 row blocks) x batch half w >> 2 (8 column
+// blocks), 128 fp32 accumulators per lane. Per matrix operation this moves
+// half the L2-to-CU bytes of the 256 x 128 wide tile.
+//  * Both operands are copied straight from memory into LDS by the load
+//    units (global_load_lds_dwordx4: each wave load fills 1 KiB of LDS, lane
+//    i at byte 16 i), one K step (32 columns) per stage, in a ring of 4
+//    stages with 3 in flight: no registers hold loads in flight.
+//    W: one wave load per row block (its K step is already 1 KiB in A-operand
+//    order). H: one wave load per 16 batch rows (64 bytes each), the four
+//    16-byte pieces of row n stored in the order q ^ ((n >> 2) & 3) so that
+//    the 16 rows a B-operand read touches fall in distinct banks.
+//  * Each wave waits for its own copies with an explicit vmcnt, then the
+//    workgroup barrier (s_barrier, no fence) publishes the stage; the LDS
+//    operand reads are written in assembly and wait for themselves, so the
+//    compiler does not insert a wait for every copy in flight before them.
+//  * Epilogue as in the wide kernel, then the four vocab quarters of each
+//    column meet in LDS.
+constexpr int kBigRows = 256, kBigCols = 256, kBigWaves = 8, kBigNS = 4;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+
+// s_waitcnt with only the vector-memory count (expcnt and lgkmcnt: no wait)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+__global__ __launch_bounds__(64 * kBigWaves) void mfma_big_kernel(Stage1Args a, int32_t n_bt) {
+  constexpr int NT = 64 * kBigWaves;
+  constexpr int W_ST = 16 * 64, H_ST = kBigCols * 4;   // uint4 per stage: W 16 KiB, H 16 KiB
+  constexpr int MJ = 4, NJ = 8;                       // row blocks, column blocks per wave
+  __shared__ uint4 lds_w[kBigNS * W_ST];
+  __shared__ uint4 lds_hb[kBigNS * H_ST];
+  __shared__ uint64_t red[4][kBigCols];
+
+  int vt, bt;
+  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int vw = wave & 3, bw = wave >> 2;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int b0 = bt * kBigCols;
+  const int D = a.D;
+  const int nC = (D + kBK - 1) / kBK;
+  const int nM = (a.V + 15) / 16;
+  const int S = D / 32;                               // K steps = stages
+  const uint4* Wt = static_cast<const uint4*>(a.W);
+  const uint16_t* H = static_cast<const uint16_t*>(a.H);
+
+  // this wave's copies of a stage: row blocks 2w, 2w + 1 of W; batch rows
+  // 32w .. 32w + 31 of H (lane: row 16 i + lane / 4, stored piece lane & 3)
+  const uint4* wsrc[2];
+  const uint16_t* hsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = min(vt * 16 + 2 * wave + i, nM - 1);
+    wsrc[i] = Wt + (((int64_t)(blk / kGroup) * nC) * kGroup + (blk % kGroup)) * kBlock16 + lane;
+    const int row = 32 * wave + 16 * i + (lane >> 2);
+    const int piece = (lane & 3) ^ ((row >> 2) & 3);
+    hsrc[i] = H + (int64_t)min(b0 + row, a.B - 1) * a.ldh + 8 * piece;
+  }
+  auto issue = [&](int st) {
+    const int c = st >> 3, t = st & 7;
+    const int buf = st % kBigNS;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      // block (blk, c) sits kGroup * kBlock16 pieces after block (blk, c - 1)
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + (int64_t)c * kGroup * kBlock16 + t * 64),
+                                       (lds_void_t*)(lds_w + buf * W_ST + (2 * wave + i) * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(hsrc[i] + 32 * st),
+                                       (lds_void_t*)(lds_hb + buf * H_ST + (2 * wave + i) * 64), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[MJ][NJ];
+#pragma unroll
+  for (int j = 0; j < MJ; ++j)
+#pragma unroll
+    for (int nb = 0; nb < NJ; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS byte addresses of this lane's operand pieces in stage buffer 0
+  uint32_t aoff[MJ], boff[NJ];
+#pragma unroll
+  for (int j = 0; j < MJ; ++j)
+    aoff[j] = (uint32_t)(uintptr_t)(lds_w + (vw * MJ + j) * 64 + lane);
+#pragma unroll
+  for (int nb = 0; nb < NJ; ++nb) {
+    const int n = bw * 128 + nb * 16 + r;
+    boff[nb] = (uint32_t)(uintptr_t)(lds_hb + n * 4 + (q ^ ((n >> 2) & 3)));
+  }
+
+  for (int st = 0; st < 3 && st < S; ++st) issue(st);
+  for (int st = 0; st < S; ++st) {
+    const int ahead = min(S - 1, st + 2) - st;        // stages issued after this one
+    if (ahead == 2) wait_vmcnt<8>();
+    else if (ahead == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();                     // stage st is in LDS for every wave
+    if (st + 3 < S) issue(st + 3);                    // into the buffer read at stage st - 1
+    const uint32_t wb = (uint32_t)((st % kBigNS) * W_ST * 16), hb = (uint32_t)((st % kBigNS) * H_ST * 16);
+    // operand reads in four chunks (A + 2 B blocks, then 2 B blocks at a
+    // time), each issued while the previous chunk's matrix instructions run
+    u32x4v av[MJ], bv[NJ];
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b128 %2, %8\n\t"
+        "ds_read_b128 %3, %9\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(av[0]), "=&v"(av[1]), "=&v"(av[2]), "=&v"(av[3]), "=&v"(bv[0]), "=&v"(bv[1])
+        : "v"(aoff[0] + wb), "v"(aoff[1] + wb), "v"(aoff[2] + wb), "v"(aoff[3] + wb),
+          "v"(boff[0] + hb), "v"(boff[1] + hb)
+        : "memory");
+#pragma unroll
+    for (int c2 = 0; c2 < NJ / 2; ++c2) {
+      if (c2 > 0) {
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b128 %1, %3\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(bv[2 * c2]), "=&v"(bv[2 * c2 + 1])
+            : "v"(boff[2 * c2] + hb), "v"(boff[2 * c2 + 1] + hb)
+            : "memory");
+      }
+#pragma unroll
+      for (int nb = 2 * c2; nb < 2 * c2 + 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < MJ; ++j)
+          acc[j][nb] = mfma16x16x32(__builtin_bit_cast(uint4, av[j]), __builtin_bit_cast(uint4, bv[nb]), acc[j][nb]);
+    }
+  }
+
+  // epilogue: per batch column, the lane's 16 candidates (4 row blocks x 4
+  // rows, increasing vocab order), then the 4 lanes of the column, then the
+  // four vocab quarters
+  auto tile_max = [&](auto greedy_c, auto full_c) {
+    constexpr bool kGreedy = decltype(greedy_c)::value;
+    constexpr bool kFull = decltype(full_c)::value;
+#pragma unroll
+    for (int nb = 0; nb < NJ; ++nb) {
+      const int col = bw * 128 + nb * 16 + r;
+      const int b = b0 + col;
+      RunMax best = runmax_init();
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
+        const int v0 = 16 * (vt * 16 + vw * MJ + j) + 4 * q;
+        uint4 words = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (!kGreedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float l = acc[j][nb][e];
+          const float sc = kGreedy ? l : score2(l, a.score_scale, pick_word(words, e));
+          if (kFull || v0 + e < a.V) runmax_take(best, sc, v0 + e);
+        }
+      }
+      uint64_t key = runmax_key(best);
+      key = umax64(key, shfl_xor_u64(key, 16));
+      key = umax64(key, shfl_xor_u64(key, 32));
+      if (q == 0) red[vw][col] = key;
+    }
+  };
+  const bool full = (int64_t)(vt + 1) * kBigRows <= a.V;
+  if (a.greedy) {
+    if (full) tile_max(std::true_type{}, std::true_type{});
+    else tile_max(std::true_type{}, std::false_type{});
+  } else {
+    if (full) tile_max(std::false_type{}, std::true_type{});
+    else tile_max(std::false_type{}, std::false_type{});
+  }
+  __syncthreads();
+  uint64_t k = 0ull;
+  if (tid < kBigCols) k = umax64(umax64(red[0][tid], red[1][tid]), umax64(red[2][tid], red[3][tid]));
+  publish_candidates(a, vt, b0, min(kBigCols, a.B - b0), k, tid, NT);
+}
+
 template <int BB, int NW>
 hipError_t launch_gemv_bb(const Stage1Args& a, hipStream_t stream) {
   const bool sample = a.cand != nullptr;
@@ -768,6 +955,20 @@ hipError_t launch_mfma_wide(const Stage1Args& a, hipStream_t stream) {
   return launch_mfma_wide_k<ROWS, false>(a, n_bt, stream);
 }
 
+// The 256 x 256 tile: tiled W with D a multiple of 32, sampling without
+// stores or log-masses (the plan checks these before choosing it).
+hipError_t launch_mfma_big(const Stage1Args& a, hipStream_t stream) {
+  const int n_bt = (a.B + kBigCols - 1) / kBigCols;
+  const int64_t G = (int64_t)a.n_tiles * n_bt;
+  const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
+  if (a.D % 32 != 0 || a.cand == nullptr || a.logits != nullptr || a.mass != nullptr)
+    return hipErrorInvalidValue;
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)G;
+  return launch(mfma_big_kernel, dim3((unsigned)grid), dim3(64 * kBigWaves), 0, stream, b, (int32_t)n_bt);
+}
+
 template <int NW, bool ROWS = false>
 hipError_t launch_mfma_nw(const Stage1Args& a, hipStream_t stream) {
   const int bn = a.batch_tile ? a.batch_tile : (a.B <= 16 ? 16 : a.B <= 32 ? 32 : 64);
@@ -805,7 +1006,8 @@ hipError_t launch_stage1_rows_direct(const Stage1Args& a, hipStream_t stream) {
 // Vocab tile = 16 rows per wave x waves per workgroup (4 or 8), or the
 // 256-row wide tile (8 waves x 2 row blocks, MFMA only).
 hipError_t launch_stage1_tiled(const Stage1Args& a, bool mfma, hipStream_t stream) {
-  if (mfma && a.vocab_tile == kWideRows) return launch_mfma_wide<false>(a, stream);
+  if (mfma && a.vocab_tile == kWideRows)
+    return a.batch_tile == kBigCols ? launch_mfma_big(a, stream) : launch_mfma_wide<false>(a, stream);
   const bool eight = a.vocab_tile == 128;
   if (mfma) return eight ? launch_mfma_nw<8>(a, stream) : launch_mfma_nw<4>(a, stream);
   return eight ? launch_gemv_nw<8>(a, stream) : launch_gemv_nw<4>(a, stream);

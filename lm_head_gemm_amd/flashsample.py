@@ -199,9 +199,9 @@ def num_vocab_tiles(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0,
 
 
 def workspace_bytes(B, D, V, dtype=torch.bfloat16, variant="auto", vocab_tile=0, tiled=False,
-                    single_pass=False, group_size=0) -> int:
+                    single_pass=False, group_size=0, batch_tile=0) -> int:
     o = make_options(variant, vocab_tile, layout=FS_LAYOUT_TILED if tiled else FS_LAYOUT_ROWS,
-                     single_pass=single_pass, group_size=group_size)
+                     single_pass=single_pass, group_size=group_size, batch_tile=batch_tile)
     return int(_lib.fs_workspace_bytes_ex(B, D, V, _dtype_code(dtype), ctypes.byref(o)))
 
 

@@ -199,6 +199,30 @@ def test_tiled_layout_validation(lib):
     o.batch_tile = 0
     o.variant = 1  # GEMV
     assert lib.fs_num_vocab_tiles(8, 4096, 1000, BF16, ctypes.byref(o)) == -1
+    # the opt-in 256 x 256 tile (batch_tile 256): tiled bf16, D a multiple of
+    # 32, plain sampling only
+    o = FsOptions()
+    o.weights_layout = 1
+    o.batch_tile = 256
+    assert lib.fs_num_vocab_tiles(300, 4096, 1000, BF16, ctypes.byref(o)) == 4
+    assert lib.fs_workspace_bytes_ex(300, 4096, 1000, BF16, ctypes.byref(o)) == 300 * 4 * 8 + 128
+    assert lib.fs_num_vocab_tiles(300, 4104, 1000, BF16, ctypes.byref(o)) == -1        # D % 32 != 0
+    o.vocab_tile = 128
+    assert lib.fs_num_vocab_tiles(300, 4096, 1000, BF16, ctypes.byref(o)) == -1
+    o.vocab_tile = 0
+    o.group_size = 1024
+    assert _fused(lib, opts=o, B=300, D=4096, V=1000, ldh=4096, ldw=4096) == UNSUPPORTED
+    o.group_size = 0
+    o.logits = FAKE
+    o.ld_logits = 1000
+    assert _fused(lib, opts=o, B=300, D=4096, V=1000, ldh=4096, ldw=4096) == UNSUPPORTED
+    o.logits = None
+    assert _fused(lib, opts=o, B=300, D=4096, V=1000, ldh=4096, ldw=4096, dtype=F32) == UNSUPPORTED
+    o.weights_layout = 0
+    assert lib.fs_num_vocab_tiles(300, 4096, 1000, BF16, ctypes.byref(o)) == -1         # row-major W
+    o.weights_layout = 1
+    ub = [FAKE, 4096, FAKE, 4096, BF16, 300, 4096, 1000, 1.0, 0, 0, F32, FAKE, 1 << 30, FAKE, None]
+    assert lib.fs_sample_unfused_ex(*ub, ctypes.byref(o)) == UNSUPPORTED
     base = [FAKE, 64, FAKE, 64, BF16, 2, 64, 1000, 1.0, 0, 0, F32, FAKE, 1 << 20, FAKE, None]
     o = FsOptions()
     o.weights_layout = 3

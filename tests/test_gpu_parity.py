@@ -458,6 +458,26 @@ def test_row_major_wide_kernel(fs, B):
     check_parity(H, W, 1.0, 4, 4, np.arange(B), tok)
 
 
+@pytest.mark.parametrize("B,D,V", [(300, 544, 3000), (513, 288, 1001), (1000, 1024, 2053), (257, 7168, 700),
+                                   (5, 256, 999)])
+def test_big_tile_parity(fs, B, D, V):
+    """The opt-in 256 x 256 tile (batch_tile 256: operands copied straight into
+    LDS; tiled layout, D a multiple of 32) with ragged V, B and K blocks:
+    every row against the oracle, greedy, single-pass, and the same tokens
+    as the default wide kernel, whose accumulation order is the same."""
+    H, W = _rand_head(B + D + V, B, D, V)
+    Hd = to_device(H)
+    tw = fs.TiledWeights(to_device(W))
+    rows = np.arange(B)
+    for T, seed, step in ((1.0, 2, 9), (0.0, 0, 0)):
+        tok = fs.sample_fused(Hd, tw, T, seed, step, batch_tile=256).cpu().numpy()
+        check_parity(H, W, T, seed, step, rows, tok)
+        one = fs.sample_fused(Hd, tw, T, seed, step, batch_tile=256, single_pass=True).cpu().numpy()
+        assert np.array_equal(tok, one)
+        wide = fs.sample_fused(Hd, tw, T, seed, step, variant="mfma", vocab_tile=256).cpu().numpy()
+        assert np.array_equal(tok, wide)
+
+
 def test_concurrent_streams_with_distinct_workspaces(fs):
     """Calls on two streams with their own workspaces and outputs overlap
     safely and give the sequential results (the header's concurrency rule)."""
