@@ -705,8 +705,9 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
 //    stages with 3 in flight: no registers hold loads in flight.
 //    W: one wave load per row block (its K step is already 1 KiB in A-operand
 //    order). H: one wave load per 16 batch rows (64 bytes each), the four
-//    16-byte pieces of row n stored in the order q ^ ((n >> 2) & 3) so that
-//    the 16 rows a B-operand read touches fall in distinct banks.
+//    16-byte pieces of row n stored in the order q ^ ((n >> 2) & 3) (the
+//    counters still show 4 bank-conflict cycles per B-operand read with it;
+//    H copied in operand order has none but its 16-row copies cost more).
 //  * Each wave waits for its own copies with an explicit vmcnt, then the
 //    workgroup barrier (s_barrier, no fence) publishes the stage; the LDS
 //    operand reads are written in assembly and wait for themselves, so the
