@@ -69,8 +69,9 @@ typedef enum fs_status {
 typedef enum fs_dtype { FS_DTYPE_BF16 = 0, FS_DTYPE_F32 = 1 } fs_dtype_t;
 
 /* Stage-1 kernel family. AUTO: GEMV (wavefront dot products) up to 2 batch
- * rows, matrix cores above (bf16: v_mfma_f32_16x16x32_bf16; fp32, row-major
- * W only: v_mfma_f32_16x16x4_f32, fp32 products and sums). */
+ * rows (up to 4 on row-major bf16 W with 4096 <= D <= 8192), matrix cores
+ * above (bf16: v_mfma_f32_16x16x32_bf16; fp32, row-major W only:
+ * v_mfma_f32_16x16x4_f32, fp32 products and sums). */
 typedef enum fs_variant { FS_VARIANT_AUTO = 0, FS_VARIANT_GEMV = 1, FS_VARIANT_MFMA = 2 } fs_variant_t;
 
 /* Layout of the W argument.

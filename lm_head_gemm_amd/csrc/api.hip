@@ -28,6 +28,19 @@ constexpr int64_t kTiledWideMinB = 65;      // batches from here on use the wide
 constexpr int32_t kMfmaSmallBTile = 64;    // one 16-row block per wave
 constexpr int32_t kMfmaLargeBTile = 128;    // two blocks per wave above 32 rows
 constexpr int64_t kGemvMaxB = 2;            // batches above this use the MFMA kernels
+// Row-major bf16 heads of hidden size kGemvLongRowD .. kGemvMaxLongRowD stay on
+// the GEMV kernel up to kGemvLongRowMaxB rows, in kGemvLongTile-row tiles (one
+// workgroup's four H rows fill at most 64 KiB of LDS); the 256-row tile also
+// serves B <= 2 from kGemvMaxLongRowD on. Measured, fused call per step: B = 3-4
+// 174-175 us against 186-187 on the 4096 x 128256 head, 288 against 304-318 on
+// 7168 x 129280, 326 against 394-404 on 8192 x 128256; B <= 2 on the 8192-wide
+// head 310-314 us against 344-348 with 16-row tiles. The 3584 x 152064 head
+// (B = 3-4: 203-251 us on GEMV, 188-196 on MFMA) and B >= 5 (600+ us: the
+// dot products then bound the GEMV kernel) stay on the matrix cores.
+constexpr int64_t kGemvLongRowD = 4096;
+constexpr int64_t kGemvMaxLongRowD = 8192;
+constexpr int64_t kGemvLongRowMaxB = 4;
+constexpr int32_t kGemvLongTile = 256;
 constexpr int32_t kSamplePart = 2048;       // unfused sampler: vocab entries per workgroup
 constexpr size_t kAlign = 256;
 // The GEMV kernels stage whole H rows in LDS (160 KiB per workgroup) next to
@@ -61,7 +74,8 @@ struct Plan {
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
 //   Row-major W: GEMV for batches up to kGemvMaxB rows (vocab tile: multiple
-//     of 16 rows), MFMA above: bf16 64 or 128 rows (with D a multiple of 256
+//     of 16 rows; bf16 heads 4096 to 8192 wide up to kGemvLongRowMaxB rows),
+//     MFMA above: bf16 64 or 128 rows (with D a multiple of 256
 //     the tiled-layout kernels read the rows directly and the 256-row wide
 //     tile is the default from 65 rows on); fp32 the fp32 matrix-core kernel
 //     (128 rows).
@@ -110,8 +124,10 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
     p->group_size = 0;
     return true;
   }
+  const bool long_rows = layout == FS_LAYOUT_ROWS && dtype == FS_DTYPE_BF16 && D >= kGemvLongRowD &&
+                         D <= kGemvMaxLongRowD && B <= kGemvLongRowMaxB;
   if (variant == FS_VARIANT_AUTO)
-    variant = B > kGemvMaxB ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
+    variant = B > kGemvMaxB && !long_rows ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
   if (variant == FS_VARIANT_MFMA && dtype == FS_DTYPE_F32 && layout == FS_LAYOUT_ROWS) {
     // fp32 matrix-core kernel: 128-row vocab tiles, batch tiles of 16, 32 or 64
     if (tile == 0) tile = mfma_f32_tile_rows();
@@ -151,7 +167,10 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
     // more rows per workgroup once the batch tile is large: fewer, longer
     // workgroups amortise staging H and the cross-wave reduction (fp32,
     // 4096 x 256 head, B = 256: 97 -> 80 us)
-    if (tile == 0) tile = B > kGemvSmallB ? kGemvLargeBTile : kGemvDefaultTile;
+    if (tile == 0) {
+      if (long_rows && (B > kGemvMaxB || D >= kGemvMaxLongRowD)) tile = kGemvLongTile;
+      else tile = B > kGemvSmallB ? kGemvLargeBTile : kGemvDefaultTile;
+    }
     if (tile < 0 || tile % kGemvGranule != 0) return false;
   }
   p->variant = (fs_variant_t)variant;

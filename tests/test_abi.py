@@ -53,6 +53,19 @@ def test_status_strings(lib):
     assert lib.fs_last_hip_error() == 0
 
 
+def test_default_plan_tile_counts(lib):
+    """Default vocab tiles per plan on row-major W (no compute): GEMV 16-row
+    tiles at B <= 2, 256-row GEMV tiles for bf16 heads 4096 to 8192 wide up to
+    four rows (and at B <= 2 from 8192 on), MFMA 64-row tiles otherwise."""
+    V = 128256
+    nt = lambda B, D, dt=BF16: lib.fs_num_vocab_tiles(B, D, V, dt, None)
+    assert nt(1, 4096) == nt(2, 7168) == math.ceil(V / 16)
+    assert nt(1, 8192) == nt(2, 8192) == math.ceil(V / 256)
+    assert nt(3, 4096) == nt(4, 7168) == nt(4, 8192) == math.ceil(V / 256)
+    assert nt(3, 3584) == nt(5, 4096) == nt(4, 8448) == math.ceil(V / 64)
+    assert nt(3, 4096, F32) != math.ceil(V / 256)     # fp32 heads keep their plans
+
+
 def test_workspace_sizes(lib):
     from lm_head_gemm_amd.flashsample import FsOptions
     nt = lib.fs_num_vocab_tiles(1, 4096, 128256, BF16, None)

@@ -99,6 +99,26 @@ def test_vocab_tile_invariance(fs, variant, tile):
     check_parity(H, W, 0.9, 3, 11, np.arange(B), got)
 
 
+@pytest.mark.parametrize("B,D,V", [(3, 4096, 3000), (4, 8192, 1001), (2, 8192, 2053), (4, 7168, 700),
+                                   (1, 8192, 257)])
+def test_long_row_gemv_plan(fs, B, D, V):
+    """Row-major bf16 heads 4096 to 8192 wide: the default plan keeps up to
+    four rows on the GEMV kernel with 256-row vocab tiles (ragged last tile);
+    every row against the oracle, single-pass equal, and the tokens equal to
+    the matrix-core kernel's on rows the margin decides."""
+    H, W = _rand_head(B * 11 + D + V, B, D, V)
+    Hd, Wd = to_device(H), to_device(W)
+    assert fs.num_vocab_tiles(B, D, V) == -(-V // 256)   # bf16
+    for T, seed, step in ((1.0, 5, 6), (0.0, 0, 0)):
+        tok = fs.sample_fused(Hd, Wd, T, seed, step).cpu().numpy()
+        check_parity(H, W, T, seed, step, np.arange(B), tok)
+        one = fs.sample_fused(Hd, Wd, T, seed, step, single_pass=True).cpu().numpy()
+        assert np.array_equal(tok, one)
+        mf = fs.sample_fused(Hd, Wd, T, seed, step, variant="mfma").cpu().numpy()
+        firm = oracle.sample(H, W, T, seed, step).margin > TOL
+        assert np.array_equal(tok[firm], mf[firm])
+
+
 @pytest.mark.parametrize("variant,tile", [("mfma", 64), ("mfma", 128), ("gemv", 64), ("gemv", 1008)])
 @pytest.mark.parametrize("B,D,V", [
     (1, 64, 5), (5, 520, 2001), (16, 256, 777), (17, 1032, 3000), (64, 4096, 2053),
