@@ -29,6 +29,18 @@ def test_philox_words_bit_exact(fs, seed, step, b, v0, n):
     assert np.array_equal(got, want)
 
 
+def test_philox_zero_counter_published_vector(fs):
+    """Seed 0, step 0, row 0, vocab 0..3 is the all-zero counter and key: the
+    device words equal the generator's published known answer (fixture)."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "philox4x32_10_kat.txt")
+    with open(path) as f:
+        zero = [l.split() for l in f if l.strip() and not l.startswith("#")][0]
+    assert all(int(w, 16) == 0 for w in zero[:6])
+    got = fs.test_philox(0, 0, 0, 0, 4).cpu().numpy().view(np.uint32)
+    assert [int(w) for w in got] == [int(w, 16) for w in zero[6:10]]
+
+
 def test_gumbel_map_accuracy(fs):
     import torch
     edge = 1 << 22

@@ -2,9 +2,9 @@
 
 The pages name no generator; the noise only has to be i.i.d. standard Gumbel
 and a function of (seed, step, row, vocab index). The oracle's generator is
-checked against an independent implementation of the same published
-generator: rocRAND's philox4x32_10 engine, compiled for the host from the
-installed ROCm headers.
+checked against the generator's published known-answer vectors and against an
+independent implementation of the same generator: rocRAND's philox4x32_10
+engine, compiled for the host from the installed ROCm headers.
 """
 import os
 import shutil
@@ -36,6 +36,22 @@ def rocrand_ref(tmp_path_factory):
                         dtype=np.uint64)
 
     return run
+
+
+def test_philox_published_known_answers():
+    """The generator's published known-answer vectors (text fixture with its
+    citation), checked on both the scalar and the vectorised path."""
+    rows = []
+    with open(os.path.join(HERE, "golden", "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                rows.append([int(w, 16) for w in line.split()])
+    assert len(rows) == 3
+    for r in rows:
+        ctr, key, want = tuple(r[0:4]), tuple(r[4:6]), tuple(r[6:10])
+        assert tuple(int(w) for w in philox4x32_10_scalar(ctr, key)) == want
+        got = philox4x32_10(*(np.array([w], dtype=np.uint64) for w in ctr + key))
+        assert tuple(int(g[0]) for g in got) == want
 
 
 def test_philox_matches_rocrand_random_counters(rocrand_ref):
