@@ -35,8 +35,9 @@ constexpr int64_t kGemvMaxB = 2;            // batches above this use the MFMA k
 // 174-175 us against 186-187 on the 4096 x 128256 head, 288 against 304-318 on
 // 7168 x 129280, 326 against 394-404 on 8192 x 128256; B <= 2 on the 8192-wide
 // head 310-314 us against 344-348 with 16-row tiles. The 3584 x 152064 head
-// (B = 3-4: 203-251 us on GEMV, 188-196 on MFMA) and B >= 5 (600+ us: the
-// dot products then bound the GEMV kernel) stay on the matrix cores.
+// (B = 3-4: 203-251 us on GEMV, 188-196 on MFMA) and B >= 5 (600+ us: eight
+// H rows per 16-byte W piece, each read from LDS and dotted, then bound the
+// GEMV kernel) stay on the matrix cores.
 constexpr int64_t kGemvLongRowD = 4096;
 constexpr int64_t kGemvMaxLongRowD = 8192;
 constexpr int64_t kGemvLongRowMaxB = 4;
