@@ -28,8 +28,8 @@
 //  * wide MFMA (B > 64): two row blocks per wave and 128-column batch tiles,
 //    H staged in sub-chunks and the B operands read one K step ahead.
 // The two MFMA kernels also serve row-major W whose D is a multiple of 256
-// (template flag ROWS): each lane then loads its A-operand piece from its
-// row instead of from the tiled copy.
+// (template flag ROWS): four neighbouring lanes then load 64 contiguous bytes
+// of a row, and a lane permutation puts the pieces in A-operand order.
 // All end in the same register epilogue: l * (1/T) + Gumbel(Philox word),
 // a running maximum per batch row, one candidate key per (row, vocab tile);
 // optionally the tile's log-mass (grouped variant) and the logits (stored
@@ -267,10 +267,22 @@ __device__ __forceinline__ void store_logits_staged(const Stage1Args& a, float* 
 }
 
 // ---------------------------------------------------------------- MFMA
+// Each lane takes the 16 bytes held by lane addr / 4 (ds_bpermute per dword).
+__device__ __forceinline__ uint4 lane_gather(const uint4& v, int addr) {
+  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w));
+}
+
 // ROWS: W is row-major [V, D] (stride ldw, D a multiple of 256) instead of
-// tiled; each lane then loads its A-operand piece straight from its row,
-// W[16m + r][256c + 32t + 8q .. +8], rows past V clamped to the last row
-// (their candidates are never valid).
+// tiled. A K step of a 16-row block is 16 runs of 64 bytes; lanes 4i .. 4i+3
+// load run i (row 16m + i, W[16m + i][256c + 32t + 8j .. +8] in lane 4i + j),
+// so neighbouring lanes read neighbouring bytes and the vector L1 serves a
+// run as one access (in operand order every lane would be its own access: 3x
+// the L1 accesses, measured), and a lane permutation then moves piece j of
+// row i to lane i + 16j, the A-operand layout. Rows past V are clamped to the
+// last row (their candidates are never valid).
 template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false, bool ROWS = false>
 __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int BN = 16 * NB;
@@ -300,7 +312,9 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   // first 16-byte piece of this lane in K block c; K step t is kTStride further
   constexpr int kTStride = ROWS ? 4 : 64;
   const uint4* wrow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.W) +
-                                                     (int64_t)min(16 * mc + r, a.V - 1) * a.ldw + 8 * q);
+                                                     (int64_t)min(16 * mc + (lane >> 2), a.V - 1) * a.ldw +
+                                                     8 * (lane & 3));
+  const int gather_addr = 4 * (4 * r + q);   // operand lane r + 16q takes run r, piece q
   const uint4* wt = static_cast<const uint4*>(a.W) + lane;
   auto wblock = [&](int c) { return ROWS ? wrow + c * (kBK / 8) : wt + block_piece(mc, c, nC); };
   // tiled: non-temporal (read once); rows: cached, so the second half of each
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
     const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow;
 #pragma unroll
     for (int t = 0; t < kKS; ++t) {
-      const uint4 x = w[t];
+      const uint4 x = ROWS ? lane_gather(w[t], gather_addr) : w[t];
       if (more) w[t] = wload(p + t * kTStride);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -473,8 +487,9 @@ constexpr int kWideBN = 16 * kWideNB;
 constexpr int kWideRows = 16 * kWideNW * kWideMB;
 
 // ROWS: row-major W [V, D] (D a multiple of 256) read directly, as in the
-// 16-rows-per-wave kernel: lane (r, q) of row block m loads
-// W[16m + r][256c + 32t + 8q .. +8], rows past V clamped.
+// 16-rows-per-wave kernel: lane 4i + j of row block m loads
+// W[16m + i][256c + 32t + 8j .. +8] (rows past V clamped), and the lane
+// permutation moves it to lane i + 16j.
 template <bool SAMPLE, bool STORE, bool MASS = false, bool ROWS = false, bool STREAMW = false>
 __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int NB = kWideNB, NW = kWideNW, MB = kWideMB, KSUB = kWideKSub, PD = kWidePD;
@@ -512,7 +527,9 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
 #pragma unroll
   for (int j = 0; j < MB; ++j)
     wrow[j] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.W) +
-                                             (int64_t)min(16 * mc[j] + r, a.V - 1) * a.ldw + 8 * q);
+                                             (int64_t)min(16 * mc[j] + (lane >> 2), a.V - 1) * a.ldw +
+                                             8 * (lane & 3));
+  const int gather_addr = 4 * (4 * r + q);   // operand lane r + 16q takes run r, piece q
   // 16-byte piece of this lane for row block j, K block c, K step t
   auto wpiece = [&](int j, int c, int t) {
     if constexpr (ROWS) return wrow[j][c * (kBK / 8) + 4 * t];
@@ -591,7 +608,7 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
         uint4 x[MB];
 #pragma unroll
         for (int j = 0; j < MB; ++j) {
-          x[j] = w[j][t % PD];
+          x[j] = ROWS ? lane_gather(w[j][t % PD], gather_addr) : w[j][t % PD];
           if (refill) w[j][t % PD] = wpiece(j, cn, tn % kKS);
         }
         if (tt + 1 < KSUB) {
