@@ -3,7 +3,7 @@ vocabulary group, then a Gumbel-max draw of the group; FlashSampling, arXiv
 2603.15854, Section 3, tensor-parallel paragraphs) against
 oracle.sample_grouped, through the C ABI: small shapes over both tiled MFMA
 kernels, ragged vocab, several batch tiles and group sizes; the reductions to
-the plain sampler; the categorical law by chi-square; full-size sampled rows.
+the plain sampler; the categorical law by chi-square (full sizes: tests/test_gpu_full_size.py).
 """
 import numpy as np
 import pytest
@@ -106,20 +106,6 @@ def test_grouped_chi_square_on_device(fs):
     p /= p.sum()
     assert counts.sum() == 10**6
     assert stats.chisquare(counts, p * 10**6).pvalue > 1e-3
-
-
-@pytest.mark.parametrize("name,B,G", [("llama3_8b", 64, 4096), ("llama3_8b", 256, 16384),
-                                      ("deepseek_v3", 16, 1024)])
-def test_grouped_full_size_sampled_rows(fs, name, B, G):
-    wl = inputs.WORKLOADS[name]
-    H = inputs.make_hidden(wl)[:B]
-    W = inputs.make_weights(wl)
-    tw = fs.TiledWeights(to_device(W))
-    tok = fs.sample_fused(to_device(H), tw, wl.temperature, wl.seed, 3, group_size=G).cpu().numpy()
-    assert tok.min() >= 0 and tok.max() < wl.V
-    rows = np.unique(np.concatenate([[0, B - 1], np.random.default_rng(wl.seed).choice(B, 6, replace=False)]))
-    n, near = check_grouped_parity(H, W, wl.temperature, wl.seed, 3, G, rows, tok[rows])
-    print(f"{name} B={B} G={G}: {n} rows checked, {near} near ties")
 
 
 @pytest.mark.parametrize("tile,G", [(64, 128), (128, 256), (256, 512)])

@@ -58,3 +58,41 @@ def test_gumbel_map_accuracy(fs):
         worst = max(worst, float(np.max(np.abs(g - ref))))
     print(f"max |g_gpu - g_fp64| = {worst:.3e}")
     assert worst <= 1e-5
+
+
+@pytest.mark.timeout(1800)
+def test_gumbel_map_every_word(fs):
+    """All 2^32 words through the device Gumbel map, each against the fp64
+    oracle: |g_gpu - g_fp64| <= 1e-5 everywhere. The device evaluates chunks
+    of 2^28 words; host threads compare slices of each chunk."""
+    import os
+    import time
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    chunk, piece = 1 << 28, 1 << 22
+    try:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        threads = 4
+
+    def compare(g, start, a):
+        words = np.arange(start + a, start + a + piece, dtype=np.uint64)
+        err = np.abs(g[a:a + piece].astype(np.float64) - oracle.gumbel_from_words(words))
+        i = int(np.argmax(err))
+        return float(err[i]), int(words[i])
+
+    worst, worst_word = 0.0, -1
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for start in range(0, 1 << 32, chunk):
+            w = torch.arange(start, start + chunk, dtype=torch.int64, device="cuda").to(torch.int32)
+            g = fs.test_gumbel(w).cpu().numpy()
+            del w
+            for e, word in ex.map(lambda a: compare(g, start, a), range(0, chunk, piece)):
+                if e > worst:
+                    worst, worst_word = e, word
+    print(f"all 2^32 words: max |g_gpu - g_fp64| = {worst:.3e} at word {worst_word:#010x} "
+          f"({time.perf_counter() - t0:.0f} s, {threads} host threads)", flush=True)
+    assert worst <= 1e-5
