@@ -9,11 +9,16 @@ kernel's achieved HBM bandwidth against MI355X's 8 TB/s (and its counter-
 measured traffic when profiles/ holds a record for these sources), and
 beside them: single-pass, the grouped variant, the unfused baseline (bf16 and
 fp32 logits) with the IO model's prediction, the row-major layout, and the
-CPU oracle's rate. --sweep adds every B of the workload, each with its HBM
-and MFMA fractions.
+CPU oracle's rate. After the headline, a compact sweep (`sweep`) times every
+workload at every B of its sweep (fewer calls per point): the fused call,
+its Stage-1 HBM and matrix-core fractions, the row-major call, single-pass
+at B <= 8, the unfused baseline, the store-logits overhead against the IO
+model and the library GEMM alone. --sweep adds every B of the headline
+workload with the headline's full detail.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--batch B] [--sweep]
                   [--layout auto|tiled|rows] [--group-size G] [--probe] [--graph]
+                  [--no-all-sweep] [--sweep-steps K] [--sweep-repeats R]
 """
 from __future__ import annotations
 
@@ -311,6 +316,61 @@ def traffic_record(kernel: str, workload: str, B: int):
     return r.get("bytes_per_launch")
 
 
+def sweep_workload(fs, wl, steps, repeats, warm_ms, vendor=True):
+    """Compact sweep entries for every B of one workload: the fused call on
+    the layout the headline uses (tiled for bf16 heads, row-major for fp32),
+    its Stage-1 HBM and matrix-core fractions, and beside it the plain call on
+    row-major W, single-pass (B <= 8), the unfused baseline (bf16 logits), the
+    store-logits option (IO-model check) and, for bf16 heads, the library GEMM
+    alone. Returns a list of dicts."""
+    import torch
+    from lm_head_gemm_amd import inputs
+    t = time.perf_counter()
+    H = inputs.make_hidden(wl)
+    W = inputs.make_weights(wl)
+    Hd = upload(H)
+    Wr = [upload(W), upload(W)]
+    del H, W
+    tiled = wl.dtype == "bf16"
+    Wt = [fs.TiledWeights(w) for w in Wr] if tiled else Wr
+    torch.cuda.synchronize()
+    log(f"[bench] sweep {wl.name}: inputs ready in {time.perf_counter() - t:.1f} s")
+    esz = 2 if wl.dtype == "bf16" else 4
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    out = []
+    for B in wl.batches:
+        Hb = Hd[:B]
+        ms, s1, _ = time_fused(fs, Hb, Wt, wl, steps, 0, B, min_warm_ms=warm_ms, repeats=repeats)
+        nt = fs.num_vocab_tiles(B, wl.D, wl.V, Hb.dtype, tiled=tiled)
+        byts = stage1_bytes(B, wl.D, wl.V, esz, nt)
+        flops = 2 * B * wl.V * wl.D
+        e = {"workload": wl.name, "B": B, "us": ms * 1e3, "samples_per_s": B / (ms * 1e-3),
+             "stage1_us": s1 * 1e3, "hbm_frac": byts / (s1 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "mfma_frac": flops / (s1 * 1e-3) / 1e12 / mfma_peak,
+             "layout": "tiled" if tiled else "rows"}
+        if tiled:
+            rms, _, _ = time_fused(fs, Hb, Wr, wl, steps, 0, B, min_warm_ms=warm_ms, repeats=repeats)
+            e["rows_us"] = rms * 1e3
+        if B <= 8:
+            sms, _, _ = time_fused(fs, Hb, Wt, wl, steps, 0, B, single_pass=True, min_warm_ms=warm_ms,
+                                   repeats=repeats)
+            e["single_pass_us"] = sms * 1e3
+        u16 = time_unfused(fs, Hb, Wt, wl, steps, 0, B, torch.bfloat16, warm_ms)
+        st = time_fused_store(fs, Hb, Wt, wl, steps, 0, B, warm_ms)
+        e.update({"unfused_us": u16 * 1e3, "fused_speedup": u16 / ms,
+                  "store_overhead": st / ms - 1.0, "store_overhead_io_model": B / wl.D,
+                  "unfused_overhead": u16 / ms - 1.0, "unfused_overhead_io_model": 2 * B / wl.D})
+        if vendor and tiled:
+            e["vendor_gemm_us"] = time_vendor_gemm(Hb, Wr, steps, 10) * 1e3
+        log(f"[bench] sweep {wl.name} B={B}: {e['us']:.1f} us (stage1 {e['stage1_us']:.1f}, "
+            f"HBM {e['hbm_frac']:.2f}, MFMA {e['mfma_frac']:.2f}), unfused {e['unfused_us']:.1f}"
+            + (f", rows {e['rows_us']:.1f}" if "rows_us" in e else ""))
+        out.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in e.items()})
+    del Hd, Wr, Wt
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,7 +381,13 @@ def main():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--batch", type=int, default=0,
                     help="batch rows per step (default: 64, or the largest of the workload's sweep below 64)")
-    ap.add_argument("--sweep", action="store_true", help="also time every B of the workload's sweep")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every B of the headline workload's sweep with the headline's full detail")
+    ap.add_argument("--no-all-sweep", action="store_true",
+                    help="skip the compact sweep over every workload and every B of its sweep")
+    ap.add_argument("--sweep-steps", type=int, default=20, help="calls per timed run in the compact sweep")
+    ap.add_argument("--sweep-repeats", type=int, default=3, help="timed runs per point in the compact sweep")
+    ap.add_argument("--sweep-workloads", default="tiny_f32,llama3_8b,qwen_7b,llama3_70b,deepseek_v3")
     ap.add_argument("--batches", default="", help="comma-separated batch sizes to sweep instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
@@ -538,7 +604,18 @@ def main():
                                  "fused_speedup": head["fused_speedup_vs_unfused_f32"]}
         result["io_model"] = head["io_model"]
     if sweep:
-        result["sweep"] = [head] + sweep
+        result["sweep_headline_workload"] = [head] + sweep
+    if not args.no_all_sweep:
+        # free the headline's buffers first: the sweep holds two copies of each head
+        del Hd, Ws
+        Ws_rows = vendor_rows = None
+        torch.cuda.empty_cache()
+        entries = []
+        for name in [x for x in args.sweep_workloads.split(",") if x]:
+            entries += sweep_workload(fs, inputs.WORKLOADS[name], args.sweep_steps, args.sweep_repeats,
+                                      min(args.min_warmup_ms, 100.0), vendor=not args.no_vendor)
+        result["sweep"] = {"steps": args.sweep_steps, "repeats": args.sweep_repeats,
+                           "layout": "tiled for bf16 heads, row-major for fp32", "entries": entries}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(H, W, wl, B)
