@@ -161,7 +161,8 @@ int32_t fs_vocab_tile_granule(fs_variant_t variant);
 /* Workspace bytes fs_sample_fused needs (candidate buffer of the Stage-1
  * tiles: one 64-bit key per (row, vocab tile); with group_size, also one fp32
  * log-mass per (row, vocab tile); with single_pass, B keys and a counter).
- * 0 on invalid sizes or options. */
+ * The size arguments come in the order of the sampling calls' own: B, D, V
+ * (batch rows, hidden size, vocabulary rows). 0 on invalid sizes or options. */
 size_t fs_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype);
 size_t fs_workspace_bytes_ex(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
                              const fs_options_t* opts);
@@ -210,7 +211,8 @@ fs_status_t fs_pack_weights_tiled(const void* W, int64_t ldw, int64_t V, int64_t
                                   void* tiled, size_t tiled_bytes, hipStream_t stream);
 
 /* Workspace of the unfused baseline: the [B, V] logits in logits_dtype plus
- * the sampler's partial candidates. 0 on invalid sizes. */
+ * the sampler's partial candidates. Size arguments B, D, V as in the sampling
+ * calls; dtype is the H and W dtype. 0 on invalid sizes. */
 size_t fs_unfused_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
                                   fs_dtype_t logits_dtype);
 

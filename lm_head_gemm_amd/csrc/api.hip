@@ -73,6 +73,13 @@ struct Plan {
   int32_t group_size = 0; // > 0: grouped variant
 };
 
+struct FusedCall {
+  Plan plan;
+  Stage1Args args;
+  size_t ws_bytes = 0;    // workspace bytes the call uses
+  bool grouped = false;   // Stage 2 of the grouped variant
+};
+
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
 //   Row-major W: GEMV for batches up to kGemvMaxB rows (vocab tile: multiple
 //     of 16 rows; bf16 heads 4096 to 8192 wide up to kGemvLongRowMaxB rows),
@@ -256,6 +263,66 @@ Stage1Args stage1_args(const void* H, int64_t ldh, const void* W, int64_t ldw, i
   return a;
 }
 
+// A validated fused call: its plan and the Stage-1 arguments with the
+// workspace carved up (candidates, log-masses or single-pass keys).
+fs_status_t prepare_fused(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype, int64_t B,
+                          int64_t D, int64_t V, float temperature, uint64_t seed, uint64_t step, void* workspace,
+                          size_t workspace_bytes, int32_t* out_tokens, const fs_options_t* opts, FusedCall* call) {
+  fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens, opts);
+  if (st != FS_OK) return st;
+  Plan& p = call->plan;
+  if (!make_plan(B, D, V, dtype, opts, &p, &st)) return st;
+  if (opts && opts->logits) {
+    if (!dtype_ok(opts->logits_dtype)) return FS_ERR_UNSUPPORTED;
+    if (opts->ld_logits < V) return FS_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)opts->logits & 15u) != 0) return FS_ERR_UNSUPPORTED;
+  }
+  call->ws_bytes = fused_ws_bytes(B, p);
+  if (workspace_bytes < call->ws_bytes) return FS_ERR_WORKSPACE_TOO_SMALL;
+
+  Stage1Args& a = call->args;
+  a = stage1_args(H, ldh, W, ldw, B, D, V, temperature, seed, step, p);
+  a.cand = static_cast<uint64_t*>(workspace);
+  call->grouped = p.group_size > 0 && !a.greedy;   // greedy: the plain maximiser
+  if (call->grouped) a.mass = reinterpret_cast<float*>(static_cast<char*>(workspace) + cand_bytes(B, p));
+  if (p.single_pass) {
+    a.single_pass = 1;
+    a.keys = static_cast<uint64_t*>(workspace);
+    a.counter = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                            align_up((size_t)B * sizeof(uint64_t), kAlign));
+    a.out = out_tokens;
+  }
+  if (opts && opts->logits) {
+    a.logits = opts->logits;
+    a.ld_logits = opts->ld_logits;
+    a.logits_bf16 = opts->logits_dtype == FS_DTYPE_BF16;
+  }
+  return FS_OK;
+}
+
+// Enqueues a prepared fused call: Stage 1 (with the optional timing events
+// around it), then Stage 2 unless it is folded into Stage 1.
+fs_status_t enqueue_fused(const FusedCall& call, fs_dtype_t dtype, int32_t* out_tokens, hipStream_t stream,
+                          const fs_options_t* opts) {
+  const Plan& p = call.plan;
+  const Stage1Args& a = call.args;
+  hipError_t e;
+  if (opts && opts->stage1_start && (e = hipEventRecord(opts->stage1_start, stream)) != hipSuccess)
+    return fail_hip(e);
+  e = launch_stage1(p, a, dtype, stream);
+  if (e != hipSuccess) return fail_hip(e);
+  if (opts && opts->stage1_stop && (e = hipEventRecord(opts->stage1_stop, stream)) != hipSuccess)
+    return fail_hip(e);
+  if (call.grouped) {
+    e = launch_stage2_grouped(a.cand, a.mass, a.B, a.n_tiles, p.group_size / p.tile, a.nk, out_tokens, stream);
+    if (e != hipSuccess) return fail_hip(e);
+  } else if (!p.single_pass) {
+    e = launch_stage2(a.cand, a.B, a.n_tiles, out_tokens, stream);
+    if (e != hipSuccess) return fail_hip(e);
+  }
+  return FS_OK;
+}
+
 }  // namespace
 }  // namespace fs
 
@@ -309,48 +376,11 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
                                int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
                                uint64_t step, void* workspace, size_t workspace_bytes,
                                int32_t* out_tokens, hipStream_t stream, const fs_options_t* opts) {
-  fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens, opts);
+  FusedCall call;
+  const fs_status_t st = prepare_fused(H, ldh, W, ldw, dtype, B, D, V, temperature, seed, step, workspace,
+                                       workspace_bytes, out_tokens, opts, &call);
   if (st != FS_OK) return st;
-  Plan p;
-  if (!make_plan(B, D, V, dtype, opts, &p, &st)) return st;
-  if (opts && opts->logits) {
-    if (!dtype_ok(opts->logits_dtype)) return FS_ERR_UNSUPPORTED;
-    if (opts->ld_logits < V) return FS_ERR_INVALID_ARGUMENT;
-    if (((uintptr_t)opts->logits & 15u) != 0) return FS_ERR_UNSUPPORTED;
-  }
-  if (workspace_bytes < fused_ws_bytes(B, p)) return FS_ERR_WORKSPACE_TOO_SMALL;
-
-  Stage1Args a = stage1_args(H, ldh, W, ldw, B, D, V, temperature, seed, step, p);
-  a.cand = static_cast<uint64_t*>(workspace);
-  const bool grouped = p.group_size > 0 && !a.greedy;   // greedy: the plain maximiser
-  if (grouped) a.mass = reinterpret_cast<float*>(static_cast<char*>(workspace) + cand_bytes(B, p));
-  if (p.single_pass) {
-    a.single_pass = 1;
-    a.keys = static_cast<uint64_t*>(workspace);
-    a.counter = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                            align_up((size_t)B * sizeof(uint64_t), kAlign));
-    a.out = out_tokens;
-  }
-  if (opts && opts->logits) {
-    a.logits = opts->logits;
-    a.ld_logits = opts->ld_logits;
-    a.logits_bf16 = opts->logits_dtype == FS_DTYPE_BF16;
-  }
-  hipError_t e;
-  if (opts && opts->stage1_start && (e = hipEventRecord(opts->stage1_start, stream)) != hipSuccess)
-    return fail_hip(e);
-  e = launch_stage1(p, a, dtype, stream);
-  if (e != hipSuccess) return fail_hip(e);
-  if (opts && opts->stage1_stop && (e = hipEventRecord(opts->stage1_stop, stream)) != hipSuccess)
-    return fail_hip(e);
-  if (grouped) {
-    e = launch_stage2_grouped(a.cand, a.mass, a.B, a.n_tiles, p.group_size / p.tile, a.nk, out_tokens, stream);
-    if (e != hipSuccess) return fail_hip(e);
-  } else if (!p.single_pass) {
-    e = launch_stage2(a.cand, a.B, a.n_tiles, out_tokens, stream);
-    if (e != hipSuccess) return fail_hip(e);
-  }
-  return FS_OK;
+  return enqueue_fused(call, dtype, out_tokens, stream, opts);
 }
 
 fs_status_t fs_sample_fused(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype,

@@ -302,3 +302,20 @@ def test_f32_matrix_core_options(lib):
     o.weights_layout = 1
     o.variant = 2
     assert _fused(lib, opts=o, dtype=F32, B=16) == UNSUPPORTED
+
+
+def test_workspace_size_argument_order(lib):
+    """The sizing calls take (B, D, V) in the order of the sampling calls'
+    size arguments (not (B, V, D)): pinned by a shape where swapping D and V
+    changes the answer."""
+    B, D, V = 2, 64, 100000
+    tiles = math.ceil(V / 16)                         # GEMV plan, 16-row vocab tiles
+    assert lib.fs_num_vocab_tiles(B, D, V, BF16, None) == tiles
+    assert lib.fs_workspace_bytes(B, D, V, BF16) == -(-B * tiles * 8 // 256) * 256
+    assert lib.fs_workspace_bytes(B, V, D, BF16) != lib.fs_workspace_bytes(B, D, V, BF16)
+    # unfused: [B, round_up(V, 8)] logits, then one key per (row, 2048-entry part)
+    logits = -(-B * (-(-V // 8) * 8) * 4 // 256) * 256
+    parts = -(-B * math.ceil(V / 2048) * 8 // 256) * 256
+    assert lib.fs_unfused_workspace_bytes(B, D, V, BF16, F32) == logits + parts
+    assert lib.fs_unfused_workspace_bytes(B, V, D, BF16, F32) != logits + parts
+
