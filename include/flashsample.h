@@ -25,7 +25,8 @@
  *
  * Conventions for every entry point below:
  *  - H, W, workspace and outputs are DEVICE pointers owned by the caller;
- *    the library allocates nothing and keeps no mutable global state.
+ *    the library allocates nothing and keeps no mutable global state (the
+ *    one exception: fs_sample_fused_noalloc's static per-GPU scratch array).
  *  - H is row-major [B, D] with row stride ldh elements, W row-major [V, D]
  *    with row stride ldw elements (ld >= D). Both have the same dtype.
  *    Base pointers must be 16-byte aligned and ld * sizeof(dtype) and
@@ -195,6 +196,29 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
                                void* workspace, size_t workspace_bytes,
                                int32_t* out_tokens, hipStream_t stream,
                                const fs_options_t* opts);
+
+/* Allocation-free fused sampler, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, results and errors as fs_sample_fused_ex
+ * without the workspace: the candidate buffer (or the single-pass keys, or
+ * the grouped variant's log-masses) lives in a static device array of
+ * FS_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held until
+ * the process ends. Its device address is looked up once per device on the
+ * first call with that device current (the stream must belong to the current
+ * device). The call allocates nothing and enqueues kernels only (single_pass
+ * adds a fill kernel that zeroes the keys first).
+ *  - Sizes whose workspace (fs_workspace_bytes_ex) exceeds
+ *    FS_NOALLOC_SCRATCH_BYTES: FS_ERR_WORKSPACE_TOO_SMALL, nothing enqueued
+ *    (e.g. V = 128256: two-stage up to B = 1024 and beyond fits).
+ *  - Every call on one GPU shares that GPU's array: calls that overlap in
+ *    time on one GPU (other streams, other threads) race and give undefined
+ *    tokens; serialise them. */
+#define FS_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+fs_status_t fs_sample_fused_noalloc(const void* H, int64_t ldh, const void* W, int64_t ldw,
+                                    fs_dtype_t dtype, int64_t B, int64_t D, int64_t V,
+                                    float temperature, uint64_t seed, uint64_t step,
+                                    int32_t* out_tokens, hipStream_t stream,
+                                    const fs_options_t* opts);
 
 /* Bytes of the tiled copy of a [V, D] bf16 LM head (V rounded up to a
  * group of 8 blocks of 16 rows, D to 256 columns, zero padded). 0 for

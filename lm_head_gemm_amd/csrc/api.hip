@@ -3,8 +3,15 @@
 // device memory; every launch goes on the caller's stream.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "fs_common.h"
+
+// Workspace of fs_sample_fused_noalloc: a static device array, one copy per
+// GPU at that GPU's own address. Host code never uses this name as an
+// address (on the host it is only a stand-in); it takes the device address
+// from hipGetSymbolAddress once per device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[FS_NOALLOC_SCRATCH_BYTES];
 
 namespace fs {
 namespace {
@@ -323,6 +330,29 @@ fs_status_t enqueue_fused(const FusedCall& call, fs_dtype_t dtype, int32_t* out_
   return FS_OK;
 }
 
+// Device address of `scratch` on the calling thread's current device, looked
+// up once per device (hipGetSymbolAddress) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // guarded by g_scratch_mutex
+
+fs_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return FS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e);
+    if (!p) return fail_hip(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FS_OK;
+}
+
 }  // namespace
 }  // namespace fs
 
@@ -380,6 +410,31 @@ fs_status_t fs_sample_fused_ex(const void* H, int64_t ldh, const void* W, int64_
   const fs_status_t st = prepare_fused(H, ldh, W, ldw, dtype, B, D, V, temperature, seed, step, workspace,
                                        workspace_bytes, out_tokens, opts, &call);
   if (st != FS_OK) return st;
+  return enqueue_fused(call, dtype, out_tokens, stream, opts);
+}
+
+fs_status_t fs_sample_fused_noalloc(const void* H, int64_t ldh, const void* W, int64_t ldw, fs_dtype_t dtype,
+                                    int64_t B, int64_t D, int64_t V, float temperature, uint64_t seed,
+                                    uint64_t step, int32_t* out_tokens, hipStream_t stream,
+                                    const fs_options_t* opts) {
+  constexpr size_t kScratchBytes = FS_NOALLOC_SCRATCH_BYTES;
+  FusedCall call;
+  // validate first (no device call), with a stand-in for the scratch address
+  fs_status_t st = prepare_fused(H, ldh, W, ldw, dtype, B, D, V, temperature, seed, step,
+                                 reinterpret_cast<void*>(kAlign), kScratchBytes, out_tokens, opts, &call);
+  if (st != FS_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != FS_OK) return st;
+  st = prepare_fused(H, ldh, W, ldw, dtype, B, D, V, temperature, seed, step, ws, kScratchBytes, out_tokens,
+                     opts, &call);
+  if (st != FS_OK) return st;
+  if (call.plan.single_pass) {
+    // the single-pass keys and counter start at zero; the array holds
+    // whatever the previous call on this GPU left (a fill kernel, not a
+    // memset, so the call stays capturable)
+    const hipError_t e = launch_fill_zero(static_cast<uint64_t*>(ws), (int64_t)(call.ws_bytes / 8), stream);
+    if (e != hipSuccess) return fail_hip(e);
+  }
   return enqueue_fused(call, dtype, out_tokens, stream, opts);
 }
 

@@ -82,6 +82,9 @@ def _load():
     lib.fs_sample_fused.argtypes = fused
     lib.fs_sample_fused_ex.restype = ctypes.c_int
     lib.fs_sample_fused_ex.argtypes = fused + [ctypes.POINTER(FsOptions)]
+    lib.fs_sample_fused_noalloc.restype = ctypes.c_int
+    lib.fs_sample_fused_noalloc.argtypes = [vp, c_i64, vp, c_i64, ctypes.c_int, c_i64, c_i64, c_i64,
+                                            ctypes.c_float, c_u64, c_u64, vp, vp, ctypes.POINTER(FsOptions)]
     lib.fs_unfused_workspace_bytes.restype = c_sz
     lib.fs_unfused_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int]
     unfused = [vp, c_i64, vp, c_i64, ctypes.c_int, c_i64, c_i64, c_i64, ctypes.c_float, c_u64, c_u64,
@@ -236,6 +239,30 @@ def sample_fused(H: torch.Tensor, W, temperature: float, seed: int, step: int,
                                  float(temperature), int(seed), int(step), workspace.data_ptr(),
                                  workspace.numel(), out.data_ptr(), _stream(stream), ctypes.byref(o))
     _check(st, "fs_sample_fused_ex")
+    return out
+
+
+# Bytes of the library's static per-GPU scratch array (FS_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def sample_fused_noalloc(H: torch.Tensor, W, temperature: float, seed: int, step: int,
+                         out: torch.Tensor | None = None, variant="auto", vocab_tile: int = 0,
+                         logits: torch.Tensor | None = None, stream=None, batch_tile: int = 0,
+                         single_pass: bool = False, group_size: int = 0) -> torch.Tensor:
+    """sample_fused without a workspace (fs_sample_fused_noalloc): the library
+    uses its static per-GPU scratch array instead, so the C call allocates
+    nothing. Calls on one GPU must not overlap in time."""
+    _check_inputs(H, W)
+    B, D = H.shape
+    wptr, ldw, V, _, layout = _weights(W)
+    o = make_options(variant, vocab_tile, logits, None, batch_tile, layout, single_pass, group_size)
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=H.device)
+    st = _lib.fs_sample_fused_noalloc(H.data_ptr(), H.stride(0), wptr, ldw, _dtype_code(H.dtype), B, D, V,
+                                      float(temperature), int(seed), int(step), out.data_ptr(), _stream(stream),
+                                      ctypes.byref(o))
+    _check(st, "fs_sample_fused_noalloc")
     return out
 
 

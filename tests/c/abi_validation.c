@@ -64,6 +64,15 @@ int main(void) {
   o.reserved = 3;
   EXPECT(fused(FAKE, 64, FAKE, 64, FS_DTYPE_BF16, 2, 64, 1000, 1.f, FAKE, 1 << 20, out, &o), FS_ERR_INVALID_ARGUMENT);
 
+  /* the allocation-free entry point validates before touching the device */
+  memset(&o, 0, sizeof o);
+  EXPECT(fs_sample_fused_noalloc(NULL, 64, FAKE, 64, FS_DTYPE_BF16, 2, 64, 1000, 1.f, 0, 0, out, NULL, &o),
+         FS_ERR_INVALID_ARGUMENT);
+  EXPECT(fs_sample_fused_noalloc(FAKE, 64, FAKE, 64, FS_DTYPE_BF16, 4096, 64, 128256, 1.f, 0, 0, out, NULL, &o),
+         FS_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(fs_sample_fused_noalloc(FAKE, 64, FAKE, 64, FS_DTYPE_BF16, 2, 64, 1000, -2.f, 0, 0, out, NULL, NULL),
+         FS_ERR_INVALID_ARGUMENT);
+
   /* unfused baseline validation */
   EXPECT(fs_sample_unfused(FAKE, 64, FAKE, 64, FS_DTYPE_BF16, 2, 64, 1000, 1.f, 0, 0, (fs_dtype_t)5, FAKE, 1 << 20,
                            out, NULL),

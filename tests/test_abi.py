@@ -319,3 +319,42 @@ def test_workspace_size_argument_order(lib):
     assert lib.fs_unfused_workspace_bytes(B, D, V, BF16, F32) == logits + parts
     assert lib.fs_unfused_workspace_bytes(B, V, D, BF16, F32) != logits + parts
 
+
+def _noalloc(lib, **kw):
+    a = dict(H=FAKE, ldh=64, W=FAKE, ldw=64, dtype=BF16, B=2, D=64, V=1000, T=1.0, seed=0, step=0,
+             out=FAKE, stream=None, opts=None)
+    a.update(kw)
+    from lm_head_gemm_amd.flashsample import FsOptions
+    o = a["opts"] if a["opts"] is not None else FsOptions()
+    return lib.fs_sample_fused_noalloc(a["H"], a["ldh"], a["W"], a["ldw"], a["dtype"], a["B"], a["D"], a["V"],
+                                       a["T"], a["seed"], a["step"], a["out"], a["stream"], ctypes.byref(o))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=None), INVALID), (dict(W=None), INVALID), (dict(out=None), INVALID), (dict(B=0), INVALID),
+    (dict(ldw=63), INVALID), (dict(T=float("nan")), INVALID), (dict(dtype=7), UNSUPPORTED),
+    (dict(H=FAKE + 2), UNSUPPORTED),
+    # candidates past the 8 MiB scratch array: 4096 rows x 8016 tiles x 8 bytes
+    (dict(B=4096, V=128256), WS_SMALL),
+])
+def test_noalloc_validation(lib, kw, status):
+    """The allocation-free entry point validates like the fused call (its
+    workspace is the static scratch array) before touching the device, and
+    refuses sizes whose workspace does not fit the array."""
+    assert _noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_fits_the_workloads(lib):
+    """Two-stage workspaces of every workload's largest batch (row-major and
+    tiled plans) fit the scratch array, and so does the grouped variant at
+    B = 1024; the first size past it is refused."""
+    from lm_head_gemm_amd.flashsample import FsOptions, NOALLOC_SCRATCH_BYTES
+    assert NOALLOC_SCRATCH_BYTES == 8 << 20
+    o = FsOptions()
+    for B, D, V in ((256, 4096, 128256), (256, 3584, 152064), (512, 8192, 128256), (1024, 7168, 129280)):
+        for layout in (0, 1):
+            o.weights_layout = layout
+            assert 0 < lib.fs_workspace_bytes_ex(B, D, V, BF16, ctypes.byref(o)) <= NOALLOC_SCRATCH_BYTES
+    o.weights_layout = 1
+    o.group_size = 16384
+    assert lib.fs_workspace_bytes_ex(1024, 7168, 129280, BF16, ctypes.byref(o)) <= NOALLOC_SCRATCH_BYTES
