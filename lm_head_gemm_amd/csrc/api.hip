@@ -32,22 +32,15 @@ constexpr int32_t kTiledWideTile = 256;     // tiled layout: 8 waves x 2 x 16 ro
 constexpr int32_t kTiledWideBatch = 128;    // batch tile of the wide kernel
 constexpr int32_t kTiledBigBatch = 256;     // opt-in 256 x 256 tile (tiled, sampling only)
 constexpr int64_t kTiledWideMinB = 65;      // batches from here on use the wide kernel
-constexpr int32_t kMfmaSmallBTile = 64;    // one 16-row block per wave
+constexpr int32_t kMfmaSmallBTile = 64;    // LDS-transposing kernel: one 16-row block per wave
 constexpr int32_t kMfmaLargeBTile = 128;    // two blocks per wave above 32 rows
+constexpr int32_t kRowsTile = 128;          // row-direct kernel (D a multiple of 256): 8 waves x 16 rows
 constexpr int64_t kGemvMaxB = 2;            // batches above this use the MFMA kernels
-// Row-major bf16 heads of hidden size kGemvLongRowD .. kGemvMaxLongRowD stay on
-// the GEMV kernel up to kGemvLongRowMaxB rows, in kGemvLongTile-row tiles (one
-// workgroup's four H rows fill at most 64 KiB of LDS); the 256-row tile also
-// serves B <= 2 from kGemvMaxLongRowD on. Measured, fused call per step: B = 3-4
-// 174-175 us against 186-187 on the 4096 x 128256 head, 288 against 304-318 on
-// 7168 x 129280, 326 against 394-404 on 8192 x 128256; B <= 2 on the 8192-wide
-// head 310-314 us against 344-348 with 16-row tiles. The 3584 x 152064 head
-// (B = 3-4: 203-251 us on GEMV, 188-196 on MFMA) and B >= 5 (600+ us: eight
-// H rows per 16-byte W piece, each read from LDS and dotted, then bound the
-// GEMV kernel) stay on the matrix cores.
-constexpr int64_t kGemvLongRowD = 4096;
-constexpr int64_t kGemvMaxLongRowD = 8192;
-constexpr int64_t kGemvLongRowMaxB = 4;
+// Row-major bf16 heads of hidden size kGemvLongRowD and more use 256-row GEMV
+// tiles up to kGemvMaxB rows (one workgroup's two H rows fill at most 32 KiB of
+// LDS). Measured, fused call per step, 8192 x 128256 head, B <= 2: 310-314 us
+// against 344-348 with 16-row tiles.
+constexpr int64_t kGemvLongRowD = 8192;
 constexpr int32_t kGemvLongTile = 256;
 constexpr int32_t kSamplePart = 2048;       // unfused sampler: vocab entries per workgroup
 constexpr size_t kAlign = 256;
@@ -89,11 +82,11 @@ struct FusedCall {
 
 // Picks the Stage-1 kernel family and vocab tile. Returns false on invalid options.
 //   Row-major W: GEMV for batches up to kGemvMaxB rows (vocab tile: multiple
-//     of 16 rows; bf16 heads 4096 to 8192 wide up to kGemvLongRowMaxB rows),
-//     MFMA above: bf16 64 or 128 rows (with D a multiple of 256
-//     the tiled-layout kernels read the rows directly and the 256-row wide
-//     tile is the default from 65 rows on); fp32 the fp32 matrix-core kernel
-//     (128 rows).
+//     of 16 rows; 256 on bf16 heads at least kGemvLongRowD wide), MFMA above:
+//     bf16 with D a multiple of 256 the row-direct kernel (128 rows) up to 64
+//     rows and the wide kernel (256 rows) from 65 on; other D the
+//     LDS-transposing kernel (64 or 128 rows); fp32 the fp32 matrix-core
+//     kernel (128 rows).
 //   Tiled W (bf16): the same split; vocab tile 64 or 128 rows (4 or 8 waves
 //     of one 16-row block each), and for MFMA batches from 65 rows on the
 //     256-row wide tile (8 waves of two blocks, batch tile 128).
@@ -139,10 +132,8 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
     p->group_size = 0;
     return true;
   }
-  const bool long_rows = layout == FS_LAYOUT_ROWS && dtype == FS_DTYPE_BF16 && D >= kGemvLongRowD &&
-                         D <= kGemvMaxLongRowD && B <= kGemvLongRowMaxB;
-  if (variant == FS_VARIANT_AUTO)
-    variant = B > kGemvMaxB && !long_rows ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
+  const bool long_rows = layout == FS_LAYOUT_ROWS && dtype == FS_DTYPE_BF16 && D >= kGemvLongRowD;
+  if (variant == FS_VARIANT_AUTO) variant = B > kGemvMaxB ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
   if (variant == FS_VARIANT_MFMA && dtype == FS_DTYPE_F32 && layout == FS_LAYOUT_ROWS) {
     // fp32 matrix-core kernel: 128-row vocab tiles, batch tiles of 16, 32 or 64
     if (tile == 0) tile = mfma_f32_tile_rows();
@@ -174,7 +165,8 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
     // D a multiple of 256: the tiled-layout kernels read the rows directly,
     // the 256-row wide tile included; other D: the transposing kernel
     const bool direct = rows_direct_ok(D);
-    if (tile == 0) tile = direct && B >= kTiledWideMinB ? kTiledWideTile : B > 32 ? kMfmaLargeBTile : kMfmaSmallBTile;
+    if (tile == 0)
+      tile = direct ? (B >= kTiledWideMinB ? kTiledWideTile : kRowsTile) : B > 32 ? kMfmaLargeBTile : kMfmaSmallBTile;
     const bool wide = direct && tile == kTiledWideTile;
     if (tile != mfma_tile_rows(1) && tile != mfma_tile_rows(2) && !wide) return false;
     if (wide != (bt == kTiledWideBatch) && bt != 0) return false;
@@ -183,7 +175,7 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
     // workgroups amortise staging H and the cross-wave reduction (fp32,
     // 4096 x 256 head, B = 256: 97 -> 80 us)
     if (tile == 0) {
-      if (long_rows && (B > kGemvMaxB || D >= kGemvMaxLongRowD)) tile = kGemvLongTile;
+      if (long_rows && B <= kGemvMaxB) tile = kGemvLongTile;
       else tile = B > kGemvSmallB ? kGemvLargeBTile : kGemvDefaultTile;
     }
     if (tile < 0 || tile % kGemvGranule != 0) return false;

@@ -27,9 +27,11 @@
 //    block per wave;
 //  * wide MFMA (B > 64): two row blocks per wave and 128-column batch tiles,
 //    H staged in sub-chunks and the B operands read one K step ahead.
-// The two MFMA kernels also serve row-major W whose D is a multiple of 256
-// (template flag ROWS): four neighbouring lanes then load 64 contiguous bytes
-// of a row, and a lane permutation puts the pieces in A-operand order.
+// Row-major W whose D is a multiple of 256 is read by two more kernels:
+// mfma_rows_kernel (B up to 64: 256-byte row runs per wave load, moved to
+// operand order through a wave-private LDS region) and the wide kernel in
+// its ROWS form (four neighbouring lanes load 64 contiguous bytes of a row, a
+// lane permutation puts the pieces in A-operand order).
 // All end in the same register epilogue: l * (1/T) + Gumbel(Philox word),
 // a running maximum per batch row, one candidate key per (row, vocab tile);
 // optionally the tile's log-mass (grouped variant) and the logits (stored
@@ -266,137 +268,30 @@ __device__ __forceinline__ void store_logits_staged(const Stage1Args& a, float* 
   __syncthreads();
 }
 
-// ---------------------------------------------------------------- MFMA
-// Each lane takes the 16 bytes held by lane addr / 4 (ds_bpermute per dword).
-__device__ __forceinline__ uint4 lane_gather(const uint4& v, int addr) {
-  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x),
-                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y),
-                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z),
-                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w));
-}
-
-// ROWS: W is row-major [V, D] (stride ldw, D a multiple of 256) instead of
-// tiled. A K step of a 16-row block is 16 runs of 64 bytes; lanes 4i .. 4i+3
-// load run i (row 16m + i, W[16m + i][256c + 32t + 8j .. +8] in lane 4i + j),
-// so neighbouring lanes read neighbouring bytes and the vector L1 serves a
-// run as one access (in operand order every lane would be its own access: 3x
-// the L1 accesses, measured), and a lane permutation then moves piece j of
-// row i to lane i + 16j, the A-operand layout. Rows past V are clamped to the
-// last row (their candidates are never valid).
-template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false, bool ROWS = false>
-__global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
+// Epilogue of the kernels in which each wave owns one 16-row block of a
+// 16 NW-row vocab tile and the workgroup one 16 NB-column batch tile: the
+// optional logits store (staged through `stage`, STAGE_BYTES of LDS the
+// main loop no longer needs), then per batch row the tile's maximiser as one
+// key (and the tile's log-mass with MASS), published for Stage 2 or the
+// single-pass reduction.
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS, int STAGE_BYTES>
+__device__ __forceinline__ void narrow_epilogue(const Stage1Args& a, const f32x4 (&acc)[NB], int vt, int b0,
+                                                float* stage, uint64_t (&red)[NW][16 * NB],
+                                                float2 (&red_mass)[MASS ? NW : 1][MASS ? 16 * NB : 1]) {
   constexpr int BN = 16 * NB;
   constexpr int NT = 64 * NW;
-  constexpr int HP = BN * (kBK / 8) / NT;   // 16-byte pieces of H per thread per block
-  static_assert(HP >= 1 && HP * NT == BN * (kBK / 8), "batch tile vs workgroup size");
-
-  __shared__ uint4 lds_h4[2 * BN * kLdsRow / 8];
-  __shared__ uint64_t red[NW][BN];
-  __shared__ float2 red_mass[MASS ? NW : 1][MASS ? BN : 1];
-  uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
-
-  int vt, bt;
-  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r = lane & 15;
   const int q = lane >> 4;
-  const int b0 = bt * BN;
-  const int D = a.D;
-  const int nC = (D + kBK - 1) / kBK;
-  const int nM = (a.V + 15) / 16;
   const int m = vt * NW + wave;
-  const int mc = min(m, nM - 1);
-  // first 16-byte piece of this lane in K block c; K step t is kTStride further
-  constexpr int kTStride = ROWS ? 4 : 64;
-  const uint4* wrow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.W) +
-                                                     (int64_t)min(16 * mc + (lane >> 2), a.V - 1) * a.ldw +
-                                                     8 * (lane & 3));
-  const int gather_addr = 4 * (4 * r + q);   // operand lane r + 16q takes run r, piece q
-  const uint4* wt = static_cast<const uint4*>(a.W) + lane;
-  auto wblock = [&](int c) { return ROWS ? wrow + c * (kBK / 8) : wt + block_piece(mc, c, nC); };
-  // tiled: non-temporal (read once); rows: cached, so the second half of each
-  // 128-byte line (the next K step's pieces) is served by the first's fetch
-  auto wload = [&](const uint4* p) { return ROWS ? *p : load_stream16(p); };
-  const uint16_t* H = static_cast<const uint16_t*>(a.H);
-
-  // This thread's share of each H block: rows hn[i], columns hk[i] .. +8;
-  // pieces past B or D are zero. (Predicated loads measured faster here than
-  // clamped-address loads followed by a select.)
-  int hn[HP], hk[HP];
-#pragma unroll
-  for (int i = 0; i < HP; ++i) {
-    const int p = tid + NT * i;
-    hn[i] = p / (kBK / 8);
-    hk[i] = 8 * (p % (kBK / 8));
-  }
-  auto load_h = [&](int c, uint4 (&h)[HP]) {
-#pragma unroll
-    for (int i = 0; i < HP; ++i) {
-      const int k = c * kBK + hk[i];
-      h[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (b0 + hn[i] < a.B && k < D) h[i] = *reinterpret_cast<const uint4*>(H + (int64_t)(b0 + hn[i]) * a.ldh + k);
-    }
-  };
-  auto store_h = [&](int buf, const uint4 (&h)[HP]) {
-#pragma unroll
-    for (int i = 0; i < HP; ++i)
-      *reinterpret_cast<uint4*>(lds_h + buf * BN * kLdsRow + hn[i] * kLdsRow + hk[i]) = h[i];
-  };
-
-  f32x4 acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Rolling prefetch: the register holding K step t of block c is reloaded
-  // with step t of block c+1 as soon as its MFMAs have been issued, so one
-  // block (8 KiB per wave) stays in flight with a single register set; W
-  // loads are unconditional (clamped row block) so the compiler can count
-  // them. H for block c+1 is loaded during block c and written to the other
-  // LDS buffer before the workgroup barrier.
-  uint4 w[kKS];
-  uint4 hreg[HP];
-  {
-    const uint4* p = wblock(0);
-#pragma unroll
-    for (int t = 0; t < kKS; ++t) w[t] = wload(p + t * kTStride);
-  }
-  load_h(0, hreg);
-  store_h(0, hreg);
-  __syncthreads();
-
-  // Block c's math; with `more`, block c+1's loads are issued on the way.
-  // The last block is peeled off so no load is ever issued for nothing.
-  auto step = [&](int c, bool more) {
-    if (more) load_h(c + 1, hreg);
-    const uint4* p = wblock(more ? c + 1 : c);
-    const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow;
-#pragma unroll
-    for (int t = 0; t < kKS; ++t) {
-      const uint4 x = ROWS ? lane_gather(w[t], gather_addr) : w[t];
-      if (more) w[t] = wload(p + t * kTStride);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
-        acc[nb] = mfma16x16x32(x, bfrag, acc[nb]);
-      }
-    }
-    if (more) {
-      store_h((c + 1) & 1, hreg);
-      __syncthreads();
-    }
-  };
-  for (int c = 0; c + 1 < nC; ++c) step(c, true);
-  step(nC - 1, false);
-
   const int v0 = 16 * m + 4 * q;   // this lane's four consecutive vocab rows
   if constexpr (STORE) {
     constexpr int NBC = NB < 2 ? NB : 2;   // 16-column blocks per staging pass
-    static_assert(16 * NBC * (16 * NW + 8) * 4 <= (int)sizeof(lds_h4), "staging tile fits the H buffers");
-    __syncthreads();                        // every wave is done reading H
-    float* T = reinterpret_cast<float*>(lds_h4);
+    static_assert(16 * NBC * (16 * NW + 8) * 4 <= STAGE_BYTES, "staging tile fits the caller's LDS");
+    __syncthreads();                        // every wave is done with the main loop's LDS
+    float* T = stage;
 #pragma unroll
     for (int p = 0; p < NB / NBC; ++p) {
       f32x4 vals[NBC];
@@ -458,6 +353,318 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
     if constexpr (MASS) publish_mass<NW>(a, red_mass, vt, b0, min(BN, a.B - b0), tid);
     publish_candidates(a, vt, b0, min(BN, a.B - b0), k, tid, NT);
   }
+}
+
+// ---------------------------------------------------------------- MFMA
+// Each lane takes the 16 bytes held by lane addr / 4 (ds_bpermute per dword).
+__device__ __forceinline__ uint4 lane_gather(const uint4& v, int addr) {
+  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.y),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.z),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w));
+}
+
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false>
+__global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
+  constexpr int BN = 16 * NB;
+  constexpr int NT = 64 * NW;
+  constexpr int HP = BN * (kBK / 8) / NT;   // 16-byte pieces of H per thread per block
+  static_assert(HP >= 1 && HP * NT == BN * (kBK / 8), "batch tile vs workgroup size");
+
+  __shared__ uint4 lds_h4[2 * BN * kLdsRow / 8];
+  __shared__ uint64_t red[NW][BN];
+  __shared__ float2 red_mass[MASS ? NW : 1][MASS ? BN : 1];
+  uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
+
+  int vt, bt;
+  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int b0 = bt * BN;
+  const int D = a.D;
+  const int nC = (D + kBK - 1) / kBK;
+  const int nM = (a.V + 15) / 16;
+  const int m = vt * NW + wave;
+  const int mc = min(m, nM - 1);
+  // first 16-byte piece of this lane in K block c; K step t is 64 pieces further
+  constexpr int kTStride = 64;
+  const uint4* wt = static_cast<const uint4*>(a.W) + lane;
+  auto wblock = [&](int c) { return wt + block_piece(mc, c, nC); };
+  auto wload = [&](const uint4* p) { return load_stream16(p); };   // read once: non-temporal
+  const uint16_t* H = static_cast<const uint16_t*>(a.H);
+
+  // This thread's share of each H block: rows hn[i], columns hk[i] .. +8;
+  // pieces past B or D are zero. (Predicated loads measured faster here than
+  // clamped-address loads followed by a select.)
+  int hn[HP], hk[HP];
+#pragma unroll
+  for (int i = 0; i < HP; ++i) {
+    const int p = tid + NT * i;
+    hn[i] = p / (kBK / 8);
+    hk[i] = 8 * (p % (kBK / 8));
+  }
+  auto load_h = [&](int c, uint4 (&h)[HP]) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      const int k = c * kBK + hk[i];
+      h[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (b0 + hn[i] < a.B && k < D) h[i] = *reinterpret_cast<const uint4*>(H + (int64_t)(b0 + hn[i]) * a.ldh + k);
+    }
+  };
+  auto store_h = [&](int buf, const uint4 (&h)[HP]) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i)
+      *reinterpret_cast<uint4*>(lds_h + buf * BN * kLdsRow + hn[i] * kLdsRow + hk[i]) = h[i];
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Rolling prefetch: the register holding K step t of block c is reloaded
+  // with step t of block c+1 as soon as its MFMAs have been issued, so one
+  // block (8 KiB per wave) stays in flight with a single register set; W
+  // loads are unconditional (clamped row block) so the compiler can count
+  // them. H for block c+1 is loaded during block c and written to the other
+  // LDS buffer before the workgroup barrier.
+  uint4 w[kKS];
+  uint4 hreg[HP];
+  {
+    const uint4* p = wblock(0);
+#pragma unroll
+    for (int t = 0; t < kKS; ++t) w[t] = wload(p + t * kTStride);
+  }
+  load_h(0, hreg);
+  store_h(0, hreg);
+  __syncthreads();
+
+  // Block c's math; with `more`, block c+1's loads are issued on the way.
+  // The last block is peeled off so no load is ever issued for nothing.
+  auto step = [&](int c, bool more) {
+    if (more) load_h(c + 1, hreg);
+    const uint4* p = wblock(more ? c + 1 : c);
+    const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow;
+#pragma unroll
+    for (int t = 0; t < kKS; ++t) {
+      const uint4 x = w[t];
+      if (more) w[t] = wload(p + t * kTStride);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t + 8 * q);
+        acc[nb] = mfma16x16x32(x, bfrag, acc[nb]);
+      }
+    }
+    if (more) {
+      store_h((c + 1) & 1, hreg);
+      __syncthreads();
+    }
+  };
+  for (int c = 0; c + 1 < nC; ++c) step(c, true);
+  step(nC - 1, false);
+
+  narrow_epilogue<NB, NW, SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, vt, b0, reinterpret_cast<float*>(lds_h4),
+                                                                     red, red_mass);
+}
+
+// ------------------------------------------------------- MFMA, row-major W
+// Row-major bf16 W [V, D] (stride ldw, D a multiple of 128), B up to 64: the
+// same tile as mfma_tiled_kernel (wave w owns row block vt * NW + w, the
+// workgroup one 16 NB-column batch tile), fed from row-major memory.
+//  * W is read in K blocks of 128 columns: per block and wave, four 16-byte
+//    non-temporal wave loads, load j covering rows 4j .. 4j+3 of the wave's
+//    block with 16 lanes (256 contiguous bytes) per row. Runs of 256 bytes
+//    per row stream from HBM about as fast as the tiled layout's (measured:
+//    6.8-6.95 TB/s against 5.8-6.3 for 64-byte runs of 16 rows).
+//  * Each wave moves its block through a private 4 KiB LDS region (16 rows x
+//    16 pieces of 16 bytes, piece p of row rho stored at p ^ rho, which keeps
+//    both the row writes and the operand reads free of bank conflicts) into
+//    the A-operand order: K step s of the block is pieces 4s .. 4s+3.
+//  * Two K blocks of W (8 KiB per wave) are in flight: block i + 2 is loaded
+//    into the registers of block i as soon as those are in LDS.
+//  * H is staged in LDS by the workgroup, 128 columns per block, double
+//    buffered, one barrier per block.
+//  * Workgroup vt starts its K loop at block vt mod (D / 128), so the
+//    workgroups in flight read different offsets of their rows: with the
+//    power-of-two row strides of 4096- and 8192-wide heads, rows read at one
+//    offset concentrate on a few memory channels (measured: 6.2 TB/s without
+//    the rotation, 6.8-6.9 with it). The accumulation order of a row's
+//    logits depends on its tile, within fp32 rounding.
+constexpr int kRowsBK = 128;               // columns per K block
+
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS>
+__global__ __launch_bounds__(64 * NW, NW / 2) void mfma_rows_kernel(Stage1Args a, int32_t n_bt) {
+  constexpr int BN = 16 * NB;
+  constexpr int NT = 64 * NW;
+  // W K blocks per H block: two (256 columns, one barrier per two W blocks)
+  // where the LDS holds it beside the W regions at two workgroups per CU
+  // (batch tiles up to 32), else one
+  constexpr int HB = NB <= 2 ? 2 : 1;
+  constexpr int HROW = HB * kRowsBK + 16;              // padded H row (elements): an odd multiple of 32 bytes
+  constexpr int HPIECES = BN * HB * (kRowsBK / 8);     // 16-byte pieces of H per H block
+  constexpr int HP = (HPIECES + NT - 1) / NT;          // per thread
+  static_assert((HROW * 2 / 32) % 2 == 1, "H row stride an odd multiple of 32 bytes");
+
+  __shared__ uint4 lds_w[NW * 16 * 16];                // per wave: 16 rows x 16 pieces
+  __shared__ uint4 lds_h4[2 * BN * HROW / 8];
+  __shared__ uint64_t red[NW][BN];
+  __shared__ float2 red_mass[MASS ? NW : 1][MASS ? BN : 1];
+  uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
+
+  int vt, bt;
+  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int b0 = bt * BN;
+  const int nM = (a.V + 15) / 16;
+  const int mc = min(vt * NW + wave, nM - 1);
+  const int nblk = a.D / kRowsBK;
+  const int s0 = vt % nblk;
+  auto blk = [&](int i) {   // i-th K block of this workgroup's rotated order (i < 2 nblk)
+    const int c = s0 + i;
+    return c >= nblk ? c - nblk : c;
+  };
+
+  // load j of a block: row 4j + q of the wave's block (clamped past V),
+  // columns 8r .. 8r+7 of the block
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  const uint16_t* wsrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wsrc[j] = W + (int64_t)min(16 * mc + 4 * j + q, a.V - 1) * a.ldw + 8 * r;
+  auto wload = [&](int c, int j) { return load_stream16(wsrc[j] + c * kRowsBK); };
+  uint4* region = lds_w + wave * 256;
+  const uint16_t* H = static_cast<const uint16_t*>(a.H);
+
+  // H block h holds the H columns of W blocks HB h .. HB h + HB - 1 side by
+  // side; this thread's pieces: row hn, W block HB h + hh, columns hk .. +8
+  int hn[HP], hh[HP], hk[HP];
+  bool hv[HP];
+#pragma unroll
+  for (int i = 0; i < HP; ++i) {
+    const int p = tid + NT * i;
+    hv[i] = p < HPIECES;
+    hn[i] = p / (HB * kRowsBK / 8);
+    const int k8 = p % (HB * kRowsBK / 8);
+    hh[i] = k8 / (kRowsBK / 8);
+    hk[i] = 8 * (k8 % (kRowsBK / 8));
+  }
+  uint4 hreg[HP];
+  auto load_h = [&](int h) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      const int wb = HB * h + hh[i];
+      hreg[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (hv[i] && b0 + hn[i] < a.B && wb < nblk)
+        hreg[i] = *reinterpret_cast<const uint4*>(H + (int64_t)(b0 + hn[i]) * a.ldh + blk(wb) * kRowsBK + hk[i]);
+    }
+  };
+  auto store_h = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i)
+      if (hv[i])
+        *reinterpret_cast<uint4*>(lds_h + buf * BN * HROW + hn[i] * HROW + hh[i] * kRowsBK + hk[i]) = hreg[i];
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // H of the first H block first, so its wait does not also wait for W;
+  // then W blocks 0 and 1 (past the last block: the last one again, unused)
+  uint4 w[2][4];
+  load_h(0);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = blk(min(k, nblk - 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[k][j] = wload(c, j);
+  }
+  store_h(0);
+  __syncthreads();
+
+  // W block i (register slot i & 1, position i % HB in its H block): into
+  // the wave's LDS region, the slot refilled with block i + 2 (REFILL); at
+  // the first block of an H block the next H block's loads are issued
+  // (HLOAD), after the last its pieces go to the other H buffer and the
+  // workgroup synchronises (HSTORE); four K steps of matrix instructions.
+  auto step = [&](int i, auto slot_c, auto refill_c, auto hload_c, auto hstore_c) {
+    constexpr int S = decltype(slot_c)::value;
+    if constexpr (decltype(hload_c)::value) load_h(i / HB + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) region[(4 * j + q) * 16 + (r ^ (4 * j + q))] = w[S][j];
+    if constexpr (decltype(refill_c)::value) {
+      const int c2 = blk(i + 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[S][j] = wload(c2, j);
+    }
+    __builtin_amdgcn_wave_barrier();   // the region's writes before this wave's reads
+    const uint16_t* hb = lds_h + ((i / HB) & 1) * BN * HROW + (HB == 2 ? S : 0) * kRowsBK;
+#pragma unroll
+    for (int t = 0; t < kRowsBK / 32; ++t) {
+      const uint4 x = region[r * 16 + ((4 * t + q) ^ r)];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * HROW + 32 * t + 8 * q);
+        acc[nb] = mfma16x16x32(x, bfrag, acc[nb]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();   // this wave's reads before the next block's writes
+    if constexpr (decltype(hstore_c)::value) {
+      store_h((i / HB + 1) & 1);
+      __syncthreads();
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  // Pairs of W blocks (i even); while blocks i .. i+3 exist every refill and
+  // H block is there. The last 1 to 3 blocks: refills only while a block is
+  // left to load, H loads only while an H block is left.
+  int i = 0;
+  for (; i + 3 < nblk; i += 2) {
+    if constexpr (HB == 2) {
+      step(i, I0{}, T{}, T{}, F{});
+      step(i + 1, I1{}, T{}, F{}, T{});
+    } else {
+      step(i, I0{}, T{}, T{}, T{});
+      step(i + 1, I1{}, T{}, T{}, T{});
+    }
+  }
+  const int left = nblk - i;
+  if constexpr (HB == 2) {
+    if (left == 3) {
+      step(i, I0{}, T{}, T{}, F{});
+      step(i + 1, I1{}, F{}, F{}, T{});
+      step(i + 2, I0{}, F{}, F{}, F{});
+    } else if (left == 2) {
+      step(i, I0{}, F{}, F{}, F{});
+      step(i + 1, I1{}, F{}, F{}, F{});
+    } else {
+      step(i, I0{}, F{}, F{}, F{});
+    }
+  } else {
+    if (left == 3) {
+      step(i, I0{}, T{}, T{}, T{});
+      step(i + 1, I1{}, F{}, T{}, T{});
+      step(i + 2, I0{}, F{}, F{}, F{});
+    } else if (left == 2) {
+      step(i, I0{}, F{}, T{}, T{});
+      step(i + 1, I1{}, F{}, F{}, F{});
+    } else {
+      step(i, I0{}, F{}, F{}, F{});
+    }
+  }
+
+  narrow_epilogue<NB, NW, SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, vt, b0, reinterpret_cast<float*>(lds_h4),
+                                                                     red, red_mass);
 }
 
 // ------------------------------------------------------- MFMA, wide tiles
@@ -925,7 +1132,7 @@ hipError_t launch_gemv_nw(const Stage1Args& a, hipStream_t stream) {
   return launch_gemv_bb<4, NW>(a, stream);
 }
 
-template <int NB, int NW, bool ROWS>
+template <int NB, int NW>
 hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   constexpr int BN = 16 * NB;
   const bool sample = a.cand != nullptr;
@@ -936,13 +1143,41 @@ hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
   void (*k)(Stage1Args, int32_t) = nullptr;
   if (a.mass)
-    k = store ? mfma_tiled_kernel<NB, NW, true, true, true, ROWS> : mfma_tiled_kernel<NB, NW, true, false, true, ROWS>;
-  else if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true, false, ROWS>;
-  else if (sample) k = mfma_tiled_kernel<NB, NW, true, false, false, ROWS>;
-  else k = mfma_tiled_kernel<NB, NW, false, true, false, ROWS>;
+    k = store ? mfma_tiled_kernel<NB, NW, true, true, true> : mfma_tiled_kernel<NB, NW, true, false, true>;
+  else if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true, false>;
+  else if (sample) k = mfma_tiled_kernel<NB, NW, true, false, false>;
+  else k = mfma_tiled_kernel<NB, NW, false, true, false>;
   Stage1Args b = a;
   b.total_wgs = (int32_t)G;
   return launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b, (int32_t)n_bt);
+}
+
+template <int NB, int NW>
+hipError_t launch_rows_nb(const Stage1Args& a, hipStream_t stream) {
+  constexpr int BN = 16 * NB;
+  const bool sample = a.cand != nullptr;
+  const bool store = a.logits != nullptr;
+  const int n_bt = (a.B + BN - 1) / BN;
+  const int64_t G = (int64_t)a.n_tiles * n_bt;
+  const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
+  if (a.D % kRowsBK != 0) return hipErrorInvalidValue;
+  void (*k)(Stage1Args, int32_t) = nullptr;
+  if (a.mass) k = store ? mfma_rows_kernel<NB, NW, true, true, true> : mfma_rows_kernel<NB, NW, true, false, true>;
+  else if (sample && store) k = mfma_rows_kernel<NB, NW, true, true, false>;
+  else if (sample) k = mfma_rows_kernel<NB, NW, true, false, false>;
+  else k = mfma_rows_kernel<NB, NW, false, true, false>;
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)G;
+  return launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b, (int32_t)n_bt);
+}
+
+template <int NW>
+hipError_t launch_rows_nw(const Stage1Args& a, hipStream_t stream) {
+  const int bn = a.batch_tile ? a.batch_tile : (a.B <= 16 ? 16 : a.B <= 32 ? 32 : 64);
+  if (bn == 16) return launch_rows_nb<1, NW>(a, stream);
+  if (bn == 32) return launch_rows_nb<2, NW>(a, stream);
+  return launch_rows_nb<4, NW>(a, stream);
 }
 
 template <bool ROWS, bool STREAMW>
@@ -987,12 +1222,12 @@ hipError_t launch_mfma_big(const Stage1Args& a, hipStream_t stream) {
   return launch(mfma_big_kernel, dim3((unsigned)grid), dim3(64 * kBigWaves), 0, stream, b, (int32_t)n_bt);
 }
 
-template <int NW, bool ROWS = false>
+template <int NW>
 hipError_t launch_mfma_nw(const Stage1Args& a, hipStream_t stream) {
   const int bn = a.batch_tile ? a.batch_tile : (a.B <= 16 ? 16 : a.B <= 32 ? 32 : 64);
-  if (bn == 16) return launch_mfma_nb<1, NW, ROWS>(a, stream);
-  if (bn == 32) return launch_mfma_nb<2, NW, ROWS>(a, stream);
-  return launch_mfma_nb<4, NW, ROWS>(a, stream);
+  if (bn == 16) return launch_mfma_nb<1, NW>(a, stream);
+  if (bn == 32) return launch_mfma_nb<2, NW>(a, stream);
+  return launch_mfma_nb<4, NW>(a, stream);
 }
 
 }  // namespace
@@ -1018,7 +1253,7 @@ bool rows_direct_ok(int64_t D) { return D % kBK == 0; }
 
 hipError_t launch_stage1_rows_direct(const Stage1Args& a, hipStream_t stream) {
   if (a.vocab_tile == kWideRows) return launch_mfma_wide<true>(a, stream);
-  return a.vocab_tile == 128 ? launch_mfma_nw<8, true>(a, stream) : launch_mfma_nw<4, true>(a, stream);
+  return a.vocab_tile == 128 ? launch_rows_nw<8>(a, stream) : launch_rows_nw<4>(a, stream);
 }
 
 // Vocab tile = 16 rows per wave x waves per workgroup (4 or 8), or the

@@ -55,15 +55,19 @@ def test_status_strings(lib):
 
 def test_default_plan_tile_counts(lib):
     """Default vocab tiles per plan on row-major W (no compute): GEMV 16-row
-    tiles at B <= 2, 256-row GEMV tiles for bf16 heads 4096 to 8192 wide up to
-    four rows (and at B <= 2 from 8192 on), MFMA 64-row tiles otherwise."""
+    tiles at B <= 2 (256-row tiles on bf16 heads 8192 wide and more), the
+    row-direct matrix-core kernel's 128-row tiles from B = 3 to 64 when D is a
+    multiple of 256, the wide kernel's 256 rows from 65 on, and the
+    LDS-transposing kernel's 64 (B <= 32) or 128 rows for other D."""
     V = 128256
     nt = lambda B, D, dt=BF16: lib.fs_num_vocab_tiles(B, D, V, dt, None)
-    assert nt(1, 4096) == nt(2, 7168) == math.ceil(V / 16)
+    assert nt(1, 4096) == nt(2, 7168) == nt(2, 3584) == math.ceil(V / 16)
     assert nt(1, 8192) == nt(2, 8192) == math.ceil(V / 256)
-    assert nt(3, 4096) == nt(4, 7168) == nt(4, 8192) == math.ceil(V / 256)
-    assert nt(3, 3584) == nt(5, 4096) == nt(4, 8448) == math.ceil(V / 64)
-    assert nt(3, 4096, F32) != math.ceil(V / 256)     # fp32 heads keep their plans
+    assert nt(3, 4096) == nt(4, 7168) == nt(4, 8192) == nt(64, 3584) == math.ceil(V / 128)
+    assert nt(65, 4096) == nt(1024, 7168) == math.ceil(V / 256)
+    assert nt(3, 4104) == nt(32, 4104) == math.ceil(V / 64)
+    assert nt(33, 4104) == math.ceil(V / 128)
+    assert nt(3, 4096, F32) == math.ceil(V / 128)     # fp32 heads: the fp32 matrix-core kernel
 
 
 def test_workspace_sizes(lib):

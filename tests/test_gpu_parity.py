@@ -99,23 +99,24 @@ def test_vocab_tile_invariance(fs, variant, tile):
 
 
 @pytest.mark.parametrize("B,D,V", [(3, 4096, 3000), (4, 8192, 1001), (2, 8192, 2053), (4, 7168, 700),
-                                   (1, 8192, 257)])
-def test_long_row_gemv_plan(fs, B, D, V):
-    """Row-major bf16 heads 4096 to 8192 wide: the default plan keeps up to
-    four rows on the GEMV kernel with 256-row vocab tiles (ragged last tile);
-    every row against the oracle, single-pass equal, and the tokens equal to
-    the matrix-core kernel's on rows the margin decides."""
+                                   (1, 8192, 257), (9, 3584, 1001), (40, 512, 4099), (64, 768, 130)])
+def test_row_major_small_batch_plans(fs, B, D, V):
+    """Row-major bf16 W: 256-row GEMV tiles at B <= 2 on heads 8192 wide, the
+    row-direct matrix-core kernel (128-row tiles, 256-byte row runs through a
+    wave-private LDS transpose, rotated K order) from B = 3 on, with ragged
+    last tiles; every row against the oracle, single-pass equal, and the
+    tokens equal to the GEMV kernel's on rows the margin decides."""
     H, W = _rand_head(B * 11 + D + V, B, D, V)
     Hd, Wd = to_device(H), to_device(W)
-    assert fs.num_vocab_tiles(B, D, V) == -(-V // 256)   # bf16
+    assert fs.num_vocab_tiles(B, D, V) == -(-V // (256 if B <= 2 else 128))   # bf16
     for T, seed, step in ((1.0, 5, 6), (0.0, 0, 0)):
         tok = fs.sample_fused(Hd, Wd, T, seed, step).cpu().numpy()
         check_parity(H, W, T, seed, step, np.arange(B), tok)
         one = fs.sample_fused(Hd, Wd, T, seed, step, single_pass=True).cpu().numpy()
         assert np.array_equal(tok, one)
-        mf = fs.sample_fused(Hd, Wd, T, seed, step, variant="mfma").cpu().numpy()
+        other = fs.sample_fused(Hd, Wd, T, seed, step, variant="gemv" if B > 2 else "mfma").cpu().numpy()
         firm = oracle.sample(H, W, T, seed, step).margin > TOL
-        assert np.array_equal(tok[firm], mf[firm])
+        assert np.array_equal(tok[firm], other[firm])
 
 
 @pytest.mark.parametrize("variant,tile", [("mfma", 64), ("mfma", 128), ("gemv", 64), ("gemv", 1008)])
