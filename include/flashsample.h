@@ -115,8 +115,10 @@ typedef struct fs_options {
   int32_t single_pass;     /* nonzero: fold Stage 2 into Stage 1 (one launch).
                               Each Stage-1 workgroup takes an atomic maximum
                               of its keys into a [B] key array in the
-                              workspace; the last workgroup to finish writes
-                              the tokens and returns the workspace to zero.
+                              workspace and counts itself finished (two
+                              levels of counters); the last workgroup to
+                              finish writes the tokens and returns the
+                              workspace to zero.
                               The workspace (fs_workspace_bytes_ex with this
                               option) must be zero before its first use
                               (fs_workspace_reset), and calls sharing it must
@@ -161,7 +163,8 @@ int32_t fs_vocab_tile_granule(fs_variant_t variant);
 
 /* Workspace bytes fs_sample_fused needs (candidate buffer of the Stage-1
  * tiles: one 64-bit key per (row, vocab tile); with group_size, also one fp32
- * log-mass per (row, vocab tile); with single_pass, B keys and a counter).
+ * log-mass per (row, vocab tile); with single_pass, B keys and the
+ * finished-workgroup counters, 8448 bytes).
  * The size arguments come in the order of the sampling calls' own: B, D, V
  * (batch rows, hidden size, vocabulary rows). 0 on invalid sizes or options. */
 size_t fs_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype);

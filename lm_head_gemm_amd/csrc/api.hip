@@ -204,7 +204,8 @@ hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, h
 size_t cand_bytes(int64_t B, const Plan& p) { return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign); }
 
 size_t fused_ws_bytes(int64_t B, const Plan& p) {
-  if (p.single_pass) return align_up((size_t)B * sizeof(uint64_t), kAlign) + kAlign;  // keys + counter
+  if (p.single_pass)   // keys + the counters, one 256-byte slot each
+    return align_up((size_t)B * sizeof(uint64_t), kAlign) + (size_t)(kSpGroups + 1) * kSpSlot * sizeof(uint32_t);
   if (p.group_size > 0) return cand_bytes(B, p) + align_up((size_t)B * (size_t)p.n_tiles * sizeof(float), kAlign);
   return cand_bytes(B, p);
 }

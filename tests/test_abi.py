@@ -180,11 +180,12 @@ def test_tiled_layout_validation(lib):
     o = FsOptions()
     o.reserved = 1
     assert _fused(lib, opts=o) == INVALID
-    # single pass: B keys + a counter, independent of the tile count
+    # single pass: B keys + 33 counter slots of 256 bytes, independent of the tile count
     o = FsOptions()
     o.single_pass = 1
-    assert lib.fs_workspace_bytes_ex(3, 64, 100000, BF16, ctypes.byref(o)) == 512
-    assert _fused(lib, opts=o, wsb=256) == WS_SMALL
+    assert lib.fs_workspace_bytes_ex(3, 64, 100000, BF16, ctypes.byref(o)) == 256 + 33 * 256
+    assert lib.fs_workspace_bytes_ex(1000, 64, 100000, BF16, ctypes.byref(o)) == 8192 + 33 * 256
+    assert _fused(lib, opts=o, wsb=256 + 33 * 256 - 1) == WS_SMALL
     assert lib.fs_workspace_reset(None, 256, None) == INVALID
     assert lib.fs_workspace_reset(FAKE, 12, None) == INVALID
     assert lib.fs_workspace_reset(FAKE + 8, 256, None) == UNSUPPORTED
