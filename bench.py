@@ -163,28 +163,6 @@ def time_fused(fs, Hb, Ws, wl, steps, warmup, B, variant="auto", vocab_tile=0, b
     return float(np.median(runs)), s1, n_warm
 
 
-def time_fused_store(fs, Hb, Ws, wl, steps, warmup, B, min_warm_ms=0.0):
-    """ms per step of the fused call with its store-logits option (bf16
-    logits written beside the sample), timed like time_fused."""
-    import torch
-    T, seed = wl.temperature, wl.seed
-    tiled = isinstance(Ws[0], fs.TiledWeights)
-    ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, tiled=tiled), dtype=torch.uint8, device="cuda")
-    out = torch.empty(B, dtype=torch.int32, device="cuda")
-    logits = torch.empty((B, wl.V), dtype=torch.bfloat16, device="cuda")
-    kw = dict(out=out, workspace=ws, logits=logits)
-    warm(lambda i: fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw), warmup, min_warm_ms)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, **kw)
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
-
-
 def time_unfused(fs, Hb, Ws, wl, steps, warmup, B, logits_dtype, min_warm_ms=0.0):
     import torch
     ws = torch.empty(fs.unfused_workspace_bytes(B, wl.D, wl.V, Hb.dtype, logits_dtype), dtype=torch.uint8,
@@ -201,6 +179,45 @@ def time_unfused(fs, Hb, Ws, wl, steps, warmup, B, logits_dtype, min_warm_ms=0.0
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+def time_interleaved(calls, steps, repeats, warm_ms):
+    """Median ms per call of each callable in `calls` (each takes the step
+    index), measured in alternating runs of `steps` calls so that every
+    variant sees the same clocks and temperature; returns a list."""
+    import torch
+    for fn in calls:
+        warm(fn, 3, warm_ms / max(1, len(calls)))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    runs = [[] for _ in calls]
+    for _ in range(max(1, repeats)):
+        for k, fn in enumerate(calls):
+            torch.cuda.synchronize()
+            t0.record()
+            for i in range(steps):
+                fn(i)
+            t1.record()
+            torch.cuda.synchronize()
+            runs[k].append(t0.elapsed_time(t1) / steps)
+    return [float(np.median(r)) for r in runs]
+
+
+def io_model_calls(fs, Hb, Ws, wl, B):
+    """The three calls of the IO-model check on one batch: the fused call,
+    the fused call that also stores bf16 logits, and the unfused baseline
+    (bf16 logits written, then read back by the sampler)."""
+    import torch
+    T, seed = wl.temperature, wl.seed
+    tiled = isinstance(Ws[0], fs.TiledWeights)
+    ws = torch.empty(fs.workspace_bytes(B, wl.D, wl.V, Hb.dtype, tiled=tiled), dtype=torch.uint8, device="cuda")
+    uws = torch.empty(fs.unfused_workspace_bytes(B, wl.D, wl.V, Hb.dtype, torch.bfloat16), dtype=torch.uint8,
+                      device="cuda")
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, wl.V), dtype=torch.bfloat16, device="cuda")
+    return [lambda i: fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, out=out, workspace=ws),
+            lambda i: fs.sample_fused(Hb, Ws[i % len(Ws)], T, seed, i, out=out, workspace=ws, logits=logits),
+            lambda i: fs.sample_unfused(Hb, Ws[i % len(Ws)], T, seed, i, torch.bfloat16, out=out, workspace=uws)]
 
 
 def time_graph(fs, Hb, Ws, wl, steps, B, reps=20):
@@ -355,11 +372,12 @@ def sweep_workload(fs, wl, steps, repeats, warm_ms, vendor=True):
             sms, _, _ = time_fused(fs, Hb, Wt, wl, steps, 0, B, single_pass=True, min_warm_ms=warm_ms,
                                    repeats=repeats)
             e["single_pass_us"] = sms * 1e3
-        u16 = time_unfused(fs, Hb, Wt, wl, steps, 0, B, torch.bfloat16, warm_ms)
-        st = time_fused_store(fs, Hb, Wt, wl, steps, 0, B, warm_ms)
+        # the IO-model check: plain, store-logits and unfused calls timed in
+        # alternating runs (like with like)
+        pl, st, u16 = time_interleaved(io_model_calls(fs, Hb, Wt, wl, B), steps, repeats, warm_ms)
         e.update({"unfused_us": u16 * 1e3, "fused_speedup": u16 / ms,
-                  "store_overhead": st / ms - 1.0, "store_overhead_io_model": B / wl.D,
-                  "unfused_overhead": u16 / ms - 1.0, "unfused_overhead_io_model": 2 * B / wl.D})
+                  "store_overhead": st / pl - 1.0, "store_overhead_io_model": B / wl.D,
+                  "unfused_overhead": u16 / pl - 1.0, "unfused_overhead_io_model": 2 * B / wl.D})
         if vendor and tiled:
             e["vendor_gemm_us"] = time_vendor_gemm(Hb, Wr, steps, 10) * 1e3
         log(f"[bench] sweep {wl.name} B={B}: {e['us']:.1f} us (stage1 {e['stage1_us']:.1f}, "
@@ -491,11 +509,15 @@ def main():
             # IO model (Section 3): with bf16 logits, the unfused path moves
             # 2*B*V*2 bytes more than the fused one (write + read back) and the
             # store-logits option B*V*2 more (write), on top of the V*D*2 of W.
-            st = time_fused_store(fs, Hb, weights, wl, args.steps, args.warmup, b, args.min_warmup_ms)
-            rec["io_model"] = {"store_logits_ms_per_step": st,
-                               "store_overhead": st / ms - 1.0,
+            # The three calls are timed in alternating runs for this comparison.
+            pl, st, ui = time_interleaved(io_model_calls(fs, Hb, weights, wl, b), args.steps, args.repeats,
+                                          args.min_warmup_ms)
+            rec["io_model"] = {"timing": "plain, store-logits and unfused calls in alternating runs",
+                               "plain_ms_per_step": pl, "store_logits_ms_per_step": st,
+                               "unfused_ms_per_step": ui,
+                               "store_overhead": st / pl - 1.0,
                                "store_overhead_predicted": b / wl.D,
-                               "unfused_overhead": u16 / ms - 1.0,
+                               "unfused_overhead": ui / pl - 1.0,
                                "unfused_overhead_predicted": 2 * b / wl.D,
                                "unfused_f32_overhead": u32 / ms - 1.0,
                                "unfused_f32_overhead_predicted": 2 * b * 4 / (wl.D * esz)}

@@ -42,7 +42,7 @@ constexpr int64_t kGemvMaxB = 2;            // batches above this use the MFMA k
 // against 344-348 with 16-row tiles.
 constexpr int64_t kGemvLongRowD = 8192;
 constexpr int32_t kGemvLongTile = 256;
-constexpr int32_t kSamplePart = 2048;       // unfused sampler: vocab entries per workgroup
+constexpr int32_t kSamplePart = 2048;       // unfused sampler: smallest part of a row per workgroup
 constexpr size_t kAlign = 256;
 // The GEMV kernels stage whole H rows in LDS (160 KiB per workgroup) next to
 // their own reduction arrays (under 1 KiB).
@@ -462,8 +462,7 @@ fs_status_t fs_sample_unfused_ex(const void* H, int64_t ldh, const void* W, int6
   const int64_t ld = unfused_ld(V);
   const size_t logits_bytes = align_up((size_t)B * ld * dtype_size(logits_dtype), kAlign);
   char* ws = static_cast<char*>(workspace);
-  uint64_t* partial = reinterpret_cast<uint64_t*>(ws + logits_bytes);
-  const int32_t n_parts = (int32_t)unfused_parts(V);
+  uint64_t* partial = reinterpret_cast<uint64_t*>(ws + logits_bytes);   // room for unfused_parts(V) per row
 
   // step 1: GEMM that writes the logits (same Stage-1 main loop, store epilogue)
   Stage1Args a = stage1_args(H, ldh, W, ldw, B, D, V, temperature, seed, step, p);
@@ -474,8 +473,9 @@ fs_status_t fs_sample_unfused_ex(const void* H, int64_t ldh, const void* W, int6
   hipError_t e = launch_stage1(p, a, dtype, stream);
   if (e != hipSuccess) return fail_hip(e);
   // step 2: sampler that reads them back
-  e = launch_sample_logits(ws, ld, a.logits_bf16, a.B, a.V, a.score_scale, a.greedy, a.nk, kSamplePart, n_parts,
-                           partial, stream);
+  int32_t n_parts = 0;
+  e = launch_sample_logits(ws, ld, a.logits_bf16, a.B, a.V, a.score_scale, a.greedy, a.nk, partial, &n_parts,
+                           stream);
   if (e != hipSuccess) return fail_hip(e);
   e = launch_stage2(partial, a.B, n_parts, out_tokens, stream);
   if (e != hipSuccess) return fail_hip(e);

@@ -391,8 +391,7 @@ hipError_t launch_stage2_grouped(const uint64_t* cand, const float* mass, int32_
                                  int32_t tiles_per_group, NoiseKey nk, int32_t* out, hipStream_t stream);
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,
                                 int32_t V, float score_scale, int32_t greedy, NoiseKey nk,
-                                int32_t part, int32_t n_parts, uint64_t* partial,
-                                hipStream_t stream);
+                                uint64_t* partial, int32_t* n_parts_out, hipStream_t stream);
 hipError_t launch_test_philox(NoiseKey nk, uint32_t b, int64_t v0, int64_t n, uint32_t* out,
                               hipStream_t stream);
 hipError_t launch_test_gumbel(const uint32_t* words, int64_t n, float* out, hipStream_t stream);

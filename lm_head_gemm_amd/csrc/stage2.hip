@@ -5,6 +5,8 @@
 // unfused baseline's sampler
 // (Gumbel-max over logits read back from device memory; the "sample from the
 // logits" step of the same section's IO model) and the noise test hooks.
+#include <type_traits>
+
 #include "fs_common.h"
 
 namespace fs {
@@ -113,43 +115,61 @@ __global__ __launch_bounds__(NT) void stage2_grouped_kernel(const uint64_t* __re
   if (tid == 0) out[row] = key_to_token(red_k[0]);
 }
 
-// Gumbel-max over materialised logits: workgroup (part, row) scans `part`
-// consecutive vocab entries of one row, four at a time (one Philox call per
-// four), and writes its best key to partial[part, row].
-template <bool BF16>
+// Gumbel-max over materialised logits: workgroup (part, row) scans `part` =
+// IT * 2048 consecutive vocab entries of one row, eight per thread per
+// chunk: every chunk's 16- or 32-byte load is issued before any arithmetic
+// (IT chunks in flight per thread), then two Philox calls per chunk (one per
+// four entries), and the workgroup's best key goes to partial[part, row].
+// Rows are ld >= V entries apart with ld a multiple of 8, so a chunk that
+// starts below V lies inside its row; entries past V are never candidates.
+template <bool BF16, int IT>
 __global__ __launch_bounds__(kThreads) void sample_logits_kernel(
     const void* __restrict__ logits, int64_t ld, int32_t V, float score_scale, int32_t greedy,
-    NoiseKey nk, int32_t part, int32_t n_parts, uint64_t* __restrict__ partial) {
+    NoiseKey nk, int32_t part, uint64_t* __restrict__ partial) {
+  constexpr int LOADS = BF16 ? 1 : 2;   // 16-byte loads per chunk of 8 entries
   __shared__ uint64_t red[kThreads / 64];
   const int row = blockIdx.y;
   const int v_begin = blockIdx.x * part;
-  const int v_end = min(V, v_begin + part);
-  uint64_t best = 0ull;
-  for (int v0 = v_begin + 4 * threadIdx.x; v0 < v_end; v0 += 4 * kThreads) {
-    float l[4];
-    if (BF16) {
-      const uint16_t* p = static_cast<const uint16_t*>(logits) + (int64_t)row * ld + v0;
-      if (v0 + 3 < v_end) {
-        const uint2 q = *reinterpret_cast<const uint2*>(p);
-        l[0] = bf16_lo(q.x); l[1] = bf16_hi(q.x); l[2] = bf16_lo(q.y); l[3] = bf16_hi(q.y);
-      } else {
-        for (int j = 0; j < 4; ++j) l[j] = v0 + j < v_end ? __uint_as_float((uint32_t)p[j] << 16) : 0.f;
-      }
-    } else {
-      const float* p = static_cast<const float*>(logits) + (int64_t)row * ld + v0;
-      if (v0 + 3 < v_end) {
-        const float4 q = *reinterpret_cast<const float4*>(p);
-        l[0] = q.x; l[1] = q.y; l[2] = q.z; l[3] = q.w;
-      } else {
-        for (int j = 0; j < 4; ++j) l[j] = v0 + j < v_end ? p[j] : 0.f;
+  uint4 raw[IT][LOADS];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int v = v_begin + (it * kThreads + (int)threadIdx.x) * 8;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      raw[it][u] = make_uint4(0u, 0u, 0u, 0u);
+      if (v < V) {
+        const char* p = static_cast<const char*>(logits) + ((int64_t)row * ld + v) * (BF16 ? 2 : 4);
+        raw[it][u] = load_stream16(p + 16 * u);
       }
     }
-    uint4 words = make_uint4(0u, 0u, 0u, 0u);
-    if (!greedy) words = philox_quad(nk, (uint32_t)(v0 >> 2), (uint32_t)row);
+  }
+  uint64_t best = 0ull;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float s = greedy ? l[j] : score2(l[j], score_scale, pick_word(words, j));
-      if (v0 + j < v_end) best = umax64(best, pack_key(s, (uint32_t)(v0 + j)));
+  for (int it = 0; it < IT; ++it) {
+    const int v = v_begin + (it * kThreads + (int)threadIdx.x) * 8;
+    float l[8];
+    if (BF16) {
+      const uint4 q = raw[it][0];
+      l[0] = bf16_lo(q.x); l[1] = bf16_hi(q.x); l[2] = bf16_lo(q.y); l[3] = bf16_hi(q.y);
+      l[4] = bf16_lo(q.z); l[5] = bf16_hi(q.z); l[6] = bf16_lo(q.w); l[7] = bf16_hi(q.w);
+    } else {
+      const uint4 q0 = raw[it][0], q1 = raw[it][LOADS - 1];
+      l[0] = __uint_as_float(q0.x); l[1] = __uint_as_float(q0.y); l[2] = __uint_as_float(q0.z);
+      l[3] = __uint_as_float(q0.w); l[4] = __uint_as_float(q1.x); l[5] = __uint_as_float(q1.y);
+      l[6] = __uint_as_float(q1.z); l[7] = __uint_as_float(q1.w);
+    }
+    if (v < V) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint4 words = make_uint4(0u, 0u, 0u, 0u);
+        if (!greedy) words = philox_quad(nk, (uint32_t)((v >> 2) + h), (uint32_t)row);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * h + j;
+          const float sc = greedy ? l[e] : score2(l[e], score_scale, pick_word(words, j));
+          if (v + e < V) best = umax64(best, pack_key(sc, (uint32_t)(v + e)));
+        }
+      }
     }
   }
 #pragma unroll
@@ -242,16 +262,34 @@ hipError_t launch_stage2_grouped(const uint64_t* cand, const float* mass, int32_
                 tiles_per_group, nk, out);
 }
 
+// Chunks per thread: as many as keep about 1024 workgroups or more over the
+// whole call (four per CU), up to eight 16-byte loads per thread in flight.
+// Returns the number of parts used (at most ceil(V / 2048)).
 hipError_t launch_sample_logits(const void* logits, int64_t ld, int32_t logits_bf16, int32_t B,
                                 int32_t V, float score_scale, int32_t greedy, NoiseKey nk,
-                                int32_t part, int32_t n_parts, uint64_t* partial,
-                                hipStream_t stream) {
+                                uint64_t* partial, int32_t* n_parts_out, hipStream_t stream) {
+  const int64_t chunks2048 = ((int64_t)V + 2047) / 2048 * B;   // 2048-entry pieces over all rows
+  int it = 1;
+  while (it < 8 && chunks2048 / (2 * it) >= 1024) it *= 2;
+  const int32_t part = 2048 * it;
+  const int32_t n_parts = (V + part - 1) / part;
+  *n_parts_out = n_parts;
   const dim3 grid(n_parts, B);
-  if (logits_bf16)
-    return launch(sample_logits_kernel<true>, grid, dim3(kThreads), 0, stream, logits, ld, V, score_scale,
-                  greedy, nk, part, n_parts, partial);
-  return launch(sample_logits_kernel<false>, grid, dim3(kThreads), 0, stream, logits, ld, V, score_scale,
-                greedy, nk, part, n_parts, partial);
+  auto go = [&](auto bf16_c, auto it_c) {
+    constexpr bool kBF16 = decltype(bf16_c)::value;
+    constexpr int kIT = decltype(it_c)::value;
+    return launch(sample_logits_kernel<kBF16, kIT>, grid, dim3(kThreads), 0, stream, logits, ld, V, score_scale,
+                  greedy, nk, part, partial);
+  };
+  auto by_it = [&](auto bf16_c) {
+    switch (it) {
+      case 1: return go(bf16_c, std::integral_constant<int, 1>{});
+      case 2: return go(bf16_c, std::integral_constant<int, 2>{});
+      case 4: return go(bf16_c, std::integral_constant<int, 4>{});
+      default: return go(bf16_c, std::integral_constant<int, 8>{});
+    }
+  };
+  return logits_bf16 ? by_it(std::true_type{}) : by_it(std::false_type{});
 }
 
 hipError_t launch_test_philox(NoiseKey nk, uint32_t b, int64_t v0, int64_t n, uint32_t* out,
