@@ -27,11 +27,12 @@
 //    block per wave;
 //  * wide MFMA (B > 64): two row blocks per wave and 128-column batch tiles,
 //    H staged in sub-chunks and the B operands read one K step ahead.
-// Row-major W whose D is a multiple of 256 is read by two more kernels:
-// mfma_rows_kernel (B up to 64: 256-byte row runs per wave load, moved to
-// operand order through a wave-private LDS region) and the wide kernel in
-// its ROWS form (four neighbouring lanes load 64 contiguous bytes of a row, a
-// lane permutation puts the pieces in A-operand order).
+// Row-major W whose D is a multiple of 256 is read by three more kernels:
+// mfma_rows_kernel (B up to 64) and mfma_rows_wide_kernel (B up to 128), with
+// 256-byte row runs per wave load moved to operand order through a
+// wave-private LDS region, and above that the wide kernel in its ROWS form
+// (four neighbouring lanes load 64 contiguous bytes of a row, a lane
+// permutation puts the pieces in A-operand order).
 // All end in the same register epilogue: l * (1/T) + Gumbel(Philox word),
 // a running maximum per batch row, one candidate key per (row, vocab tile);
 // optionally the tile's log-mass (grouped variant) and the logits (stored
@@ -693,6 +694,103 @@ constexpr int kWidePD = 4;                     // W prefetch distance in K steps
 constexpr int kWideBN = 16 * kWideNB;
 constexpr int kWideRows = 16 * kWideNW * kWideMB;
 
+// Epilogue of the wide tile (wave w owns row blocks m[j] = vt * NW * MB + j * NW
+// + w, j < MB, of a 16 NW MB-row vocab tile; the workgroup one 16 NB-column batch
+// tile): the optional logits store staged through `stage` (STAGE_BYTES of LDS
+// the main loop no longer needs), then per batch row the tile's maximiser as
+// one key (and the tile's log-mass with MASS), published for Stage 2 or the
+// single-pass reduction.
+template <bool SAMPLE, bool STORE, bool MASS, int STAGE_BYTES>
+__device__ __forceinline__ void wide_epilogue(const Stage1Args& a, const f32x4 (&acc)[kWideMB][kWideNB],
+                                              const int (&m)[kWideMB], int vt, int b0, float* stage,
+                                              uint64_t (&red)[kWideNW][kWideBN],
+                                              float2 (&red_mass)[MASS ? kWideNW : 1][MASS ? kWideBN : 1]) {
+  constexpr int NB = kWideNB, NW = kWideNW, MB = kWideMB, BN = kWideBN, NT = 64 * NW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  if constexpr (STORE) {
+    constexpr int NBC = 2;                  // 16-column blocks per staging pass
+    static_assert(16 * NBC * (16 * NW + 8) * 4 <= STAGE_BYTES, "staging tile fits the caller's LDS");
+    __syncthreads();                        // every wave is done with the main loop's LDS
+    float* T = stage;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+#pragma unroll
+      for (int p = 0; p < NB / NBC; ++p) {
+        f32x4 vals[NBC];
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) vals[i] = acc[j][p * NBC + i];
+        store_logits_staged<NW, NBC>(a, T, 16 * (vt * NW * MB + j * NW), b0 + p * NBC * 16, vals, tid);
+      }
+    }
+  }
+  if constexpr (SAMPLE) {
+    // Per batch column: the lane's 4 x MB candidates come in increasing
+    // vocab order (a running maximum suffices), then the four lanes of the
+    // column combine their keys. Batch columns past B are computed on zero
+    // rows and dropped by publish_candidates. Only the last vocab tile needs
+    // the bound check on v; greedy (T = 0) skips the noise entirely.
+    auto tile_max = [&](auto greedy_c, auto full_c) {
+      constexpr bool kGreedy = decltype(greedy_c)::value;
+      constexpr bool kFull = decltype(full_c)::value;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int b = b0 + nb * 16 + r;
+        RunMax best = runmax_init();
+#pragma unroll
+        for (int j = 0; j < MB; ++j) {
+          const int v0 = 16 * m[j] + 4 * q;   // this lane's four consecutive vocab rows
+          uint4 words = make_uint4(0u, 0u, 0u, 0u);
+          if constexpr (!kGreedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float l = acc[j][nb][e];
+            const float sc = kGreedy ? l : score2(l, a.score_scale, pick_word(words, e));
+            if (kFull || v0 + e < a.V) runmax_take(best, sc, v0 + e);
+          }
+        }
+        uint64_t key = runmax_key(best);
+        key = umax64(key, shfl_xor_u64(key, 16));
+        key = umax64(key, shfl_xor_u64(key, 32));
+        if (q == 0) red[wave][nb * 16 + r] = key;
+        if constexpr (MASS && !kGreedy) {
+          float x[4 * MB], mx = -__builtin_inff(), sm = 0.f;
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 16 * m[j] + 4 * q + e;
+              x[4 * j + e] = (kFull || v < a.V) ? acc[j][nb][e] * a.inv_t : __builtin_nanf("");
+              mx = fmaxf(mx, x[4 * j + e]);   // NaN entries are skipped
+            }
+          lane_mass(x, mx, sm);
+          mass_reduce_store(red_mass[wave], nb * 16 + r, q, mx, sm);
+        }
+      }
+    };
+    const bool full = (int64_t)(vt + 1) * kWideRows <= a.V;
+    if (a.greedy) {
+      if (full) tile_max(std::true_type{}, std::true_type{});
+      else tile_max(std::true_type{}, std::false_type{});
+    } else {
+      if (full) tile_max(std::false_type{}, std::true_type{});
+      else tile_max(std::false_type{}, std::false_type{});
+    }
+    __syncthreads();
+    uint64_t k = 0ull;
+    if (tid < BN) {
+      k = red[0][tid];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) k = umax64(k, red[w2][tid]);
+    }
+    if constexpr (MASS) publish_mass<NW>(a, red_mass, vt, b0, min(BN, a.B - b0), tid);
+    publish_candidates(a, vt, b0, min(BN, a.B - b0), k, tid, NT);
+  }
+}
+
 // ROWS: row-major W [V, D] (D a multiple of 256) read directly, as in the
 // 16-rows-per-wave kernel: lane 4i + j of row block m loads
 // W[16m + i][256c + 32t + 8j .. +8] (rows past V clamped), and the lane
@@ -835,84 +933,148 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
   for (int c = 0; c + 1 < nC; ++c) step(c, false);
   step(nC - 1, true);
 
-  if constexpr (STORE) {
-    constexpr int NBC = 2;                  // 16-column blocks per staging pass
-    static_assert(16 * NBC * (16 * NW + 8) * 4 <= (int)sizeof(lds_h4), "staging tile fits the H buffers");
-    __syncthreads();                        // every wave is done reading H
-    float* T = reinterpret_cast<float*>(lds_h4);
+  wide_epilogue<SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, m, vt, b0, reinterpret_cast<float*>(lds_h4), red,
+                                                         red_mass);
+}
+
+// ------------------------------------------------------- MFMA, row-major W, wide tiles
+// Row-major bf16 W (D a multiple of 128), 64 < B <= 128: the wide tile (wave w owns
+// row blocks m[j] = vt * 16 + j * 8 + w, j < 2: 256 vocab rows; the
+// workgroup one 128-column batch tile) fed like mfma_rows_kernel: per
+// 128-column K block and wave, eight 16-byte wave loads of 4 rows x 256
+// contiguous bytes (one K block in flight), each wave's two row blocks moved
+// to operand order through a private 8 KiB LDS region (piece p of row rho at
+// p ^ rho), H staged per K block and double buffered, one barrier per K
+// block, the K loop of workgroup (vt, bt) starting at block vt mod (D / 128).
+// W loads are non-temporal with one or two batch tiles (the second reads the
+// caches right after the first) and cached with more (later batch tiles of
+// the vocab tile re-read W from L2); the plan uses it for one batch tile.
+template <bool SAMPLE, bool STORE, bool MASS, bool STREAMW>
+__global__ __launch_bounds__(64 * kWideNW) void mfma_rows_wide_kernel(Stage1Args a, int32_t n_bt) {
+  constexpr int NB = kWideNB, NW = kWideNW, MB = kWideMB, BN = kWideBN, NT = 64 * NW;
+  constexpr int HROW = kRowsBK + 16;                   // padded H row (elements): 288 bytes
+  constexpr int HPIECES = BN * (kRowsBK / 8);
+  constexpr int HP = HPIECES / NT;
+  static_assert(HP * NT == HPIECES, "H pieces per thread");
+
+  __shared__ uint4 lds_w[NW * MB * 16 * 16];           // per wave: MB blocks x 16 rows x 16 pieces
+  __shared__ uint4 lds_h4[2 * BN * HROW / 8];
+  __shared__ uint64_t red[NW][BN];
+  __shared__ float2 red_mass[MASS ? NW : 1][MASS ? BN : 1];
+  uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
+
+  int vt, bt;
+  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int b0 = bt * BN;
+  const int nM = (a.V + 15) / 16;
+  int m[MB];
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
+  for (int j = 0; j < MB; ++j) m[j] = vt * NW * MB + j * NW + wave;
+  const int nblk = a.D / kRowsBK;
+  const int s0 = vt % nblk;
+  auto blk = [&](int i) {   // i-th K block of this workgroup's rotated order (i < 2 nblk)
+    const int c = s0 + i;
+    return c >= nblk ? c - nblk : c;
+  };
+
+  // load (j, i) of a block: row 4i + q of row block j (clamped past V), columns 8r .. 8r+7
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  const uint16_t* wsrc[MB][4];
 #pragma unroll
-      for (int p = 0; p < NB / NBC; ++p) {
-        f32x4 vals[NBC];
+  for (int j = 0; j < MB; ++j)
 #pragma unroll
-        for (int i = 0; i < NBC; ++i) vals[i] = acc[j][p * NBC + i];
-        store_logits_staged<NW, NBC>(a, T, 16 * (vt * NW * MB + j * NW), b0 + p * NBC * 16, vals, tid);
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      wsrc[j][i] = W + (int64_t)min(16 * min(m[j], nM - 1) + 4 * i + q, a.V - 1) * a.ldw + 8 * r;
+  auto wload = [&](int c, int j, int i) {
+    if constexpr (STREAMW) return load_stream16(wsrc[j][i] + c * kRowsBK);
+    else return *reinterpret_cast<const uint4*>(wsrc[j][i] + c * kRowsBK);
+  };
+  uint4* region = lds_w + wave * MB * 256;
+  const uint16_t* H = static_cast<const uint16_t*>(a.H);
+
+  int hn[HP], hk[HP];
+#pragma unroll
+  for (int i = 0; i < HP; ++i) {
+    const int p = tid + NT * i;
+    hn[i] = p / (kRowsBK / 8);
+    hk[i] = 8 * (p % (kRowsBK / 8));
   }
-  if constexpr (SAMPLE) {
-    // Per batch column: the lane's 4 x MB candidates come in increasing
-    // vocab order (a running maximum suffices), then the four lanes of the
-    // column combine their keys. Batch columns past B are computed on zero
-    // rows and dropped by publish_candidates. Only the last vocab tile needs
-    // the bound check on v; greedy (T = 0) skips the noise entirely.
-    auto tile_max = [&](auto greedy_c, auto full_c) {
-      constexpr bool kGreedy = decltype(greedy_c)::value;
-      constexpr bool kFull = decltype(full_c)::value;
+  uint4 hreg[HP];
+  auto load_h = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      hreg[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (b0 + hn[i] < a.B)
+        hreg[i] = *reinterpret_cast<const uint4*>(H + (int64_t)(b0 + hn[i]) * a.ldh + c * kRowsBK + hk[i]);
+    }
+  };
+  auto store_h = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i)
+      *reinterpret_cast<uint4*>(lds_h + buf * BN * HROW + hn[i] * HROW + hk[i]) = hreg[i];
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // H of the first block first, so its wait does not also wait for W; then
+  // W block 0. One K block of W (8 KiB per wave) stays in flight: block i + 1
+  // is loaded into the registers of block i as soon as those are in LDS.
+  uint4 w[MB][4];
+  load_h(blk(0));
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[j][k] = wload(blk(0), j, k);
+  store_h(0);
+  __syncthreads();
+
+  for (int i = 0; i < nblk; ++i) {
+    const bool more = i + 1 < nblk;
+    if (more) load_h(blk(i + 1));
+#pragma unroll
+    for (int j = 0; j < MB; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) region[(16 * j + 4 * k + q) * 16 + (r ^ (4 * k + q))] = w[j][k];
+    {
+      const int c2 = blk(more ? i + 1 : i);   // the last block reloads itself (in bounds, unused)
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[j][k] = wload(c2, j, k);
+    }
+    __builtin_amdgcn_wave_barrier();   // the region's writes before this wave's reads
+    const uint16_t* hb = lds_h + (i & 1) * BN * HROW;
+#pragma unroll
+    for (int t = 0; t < kRowsBK / 32; ++t) {
+      uint4 x[MB];
+#pragma unroll
+      for (int j = 0; j < MB; ++j) x[j] = region[(16 * j + r) * 16 + ((4 * t + q) ^ r)];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int b = b0 + nb * 16 + r;
-        RunMax best = runmax_init();
+        const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * HROW + 32 * t + 8 * q);
 #pragma unroll
-        for (int j = 0; j < MB; ++j) {
-          const int v0 = 16 * m[j] + 4 * q;   // this lane's four consecutive vocab rows
-          uint4 words = make_uint4(0u, 0u, 0u, 0u);
-          if constexpr (!kGreedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float l = acc[j][nb][e];
-            const float sc = kGreedy ? l : score2(l, a.score_scale, pick_word(words, e));
-            if (kFull || v0 + e < a.V) runmax_take(best, sc, v0 + e);
-          }
-        }
-        uint64_t key = runmax_key(best);
-        key = umax64(key, shfl_xor_u64(key, 16));
-        key = umax64(key, shfl_xor_u64(key, 32));
-        if (q == 0) red[wave][nb * 16 + r] = key;
-        if constexpr (MASS && !kGreedy) {
-          float x[4 * MB], mx = -__builtin_inff(), sm = 0.f;
-#pragma unroll
-          for (int j = 0; j < MB; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int v = 16 * m[j] + 4 * q + e;
-              x[4 * j + e] = (kFull || v < a.V) ? acc[j][nb][e] * a.inv_t : __builtin_nanf("");
-              mx = fmaxf(mx, x[4 * j + e]);   // NaN entries are skipped
-            }
-          lane_mass(x, mx, sm);
-          mass_reduce_store(red_mass[wave], nb * 16 + r, q, mx, sm);
-        }
+        for (int j = 0; j < MB; ++j) acc[j][nb] = mfma16x16x32(x[j], bfrag, acc[j][nb]);
       }
-    };
-    const bool full = (int64_t)(vt + 1) * kWideRows <= a.V;
-    if (a.greedy) {
-      if (full) tile_max(std::true_type{}, std::true_type{});
-      else tile_max(std::true_type{}, std::false_type{});
-    } else {
-      if (full) tile_max(std::false_type{}, std::true_type{});
-      else tile_max(std::false_type{}, std::false_type{});
     }
-    __syncthreads();
-    uint64_t k = 0ull;
-    if (tid < BN) {
-      k = red[0][tid];
-#pragma unroll
-      for (int w2 = 1; w2 < NW; ++w2) k = umax64(k, red[w2][tid]);
+    __builtin_amdgcn_wave_barrier();   // this wave's reads before the next block's writes
+    if (more) {
+      store_h((i + 1) & 1);
+      __syncthreads();
     }
-    if constexpr (MASS) publish_mass<NW>(a, red_mass, vt, b0, min(BN, a.B - b0), tid);
-    publish_candidates(a, vt, b0, min(BN, a.B - b0), k, tid, NT);
   }
+
+  wide_epilogue<SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, m, vt, b0, reinterpret_cast<float*>(lds_h4), red,
+                                                         red_mass);
 }
 
 // ------------------------------------------------------- MFMA, 256 x 256 tiles
@@ -1236,6 +1398,30 @@ hipError_t launch_mfma_wide_k(const Stage1Args& a, int n_bt, hipStream_t stream)
   return launch(k, dim3((unsigned)grid), dim3(64 * kWideNW), 0, stream, b, (int32_t)n_bt);
 }
 
+template <bool STREAMW>
+hipError_t launch_rows_wide_k(const Stage1Args& a, int n_bt, hipStream_t stream) {
+  const bool sample = a.cand != nullptr;
+  const bool store = a.logits != nullptr;
+  const int64_t G = (int64_t)a.n_tiles * n_bt;
+  const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
+  if (a.D % kRowsBK != 0) return hipErrorInvalidValue;
+  void (*k)(Stage1Args, int32_t) = nullptr;
+  if (a.mass)
+    k = store ? mfma_rows_wide_kernel<true, true, true, STREAMW> : mfma_rows_wide_kernel<true, false, true, STREAMW>;
+  else if (sample && store) k = mfma_rows_wide_kernel<true, true, false, STREAMW>;
+  else if (sample) k = mfma_rows_wide_kernel<true, false, false, STREAMW>;
+  else k = mfma_rows_wide_kernel<false, true, false, STREAMW>;
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)G;
+  return launch(k, dim3((unsigned)grid), dim3(64 * kWideNW), 0, stream, b, (int32_t)n_bt);
+}
+
+hipError_t launch_rows_wide(const Stage1Args& a, hipStream_t stream) {
+  const int n_bt = (a.B + kWideBN - 1) / kWideBN;
+  return n_bt <= 2 ? launch_rows_wide_k<true>(a, n_bt, stream) : launch_rows_wide_k<false>(a, n_bt, stream);
+}
+
 // Tiled W read by at most two batch tiles streams past the caches; row-major
 // W keeps cached loads (the second half of each 128-byte line is the next K
 // step's).
@@ -1290,7 +1476,12 @@ hipError_t launch_pack_tiled(const void* W, int64_t ldw, int32_t V, int32_t D, v
 bool rows_direct_ok(int64_t D) { return D % kBK == 0; }
 
 hipError_t launch_stage1_rows_direct(const Stage1Args& a, hipStream_t stream) {
-  if (a.vocab_tile == kWideRows) return launch_mfma_wide<true>(a, stream);
+  // wide tile: the LDS-transposing row kernel for one batch tile (B <= 128),
+  // the row-direct wide kernel above (measured, 4096 x 128256 head: B = 128
+  // 200 us against 248-254; B = 256 360 against 329-333, where the matrix
+  // cores bound the loop and the extra LDS traffic of the transpose costs)
+  if (a.vocab_tile == kWideRows)
+    return a.B <= kWideBN ? launch_rows_wide(a, stream) : launch_mfma_wide<true>(a, stream);
   return a.vocab_tile == 128 ? launch_rows_nw<8>(a, stream) : launch_rows_nw<4>(a, stream);
 }
 

@@ -439,9 +439,12 @@ def test_chi_square_on_device(fs):
 
 @pytest.mark.parametrize("B", [65, 150, 300])
 def test_row_major_wide_kernel(fs, B):
-    """Row-major W with D a multiple of 256 above 64 rows: the wide kernel reads
-    the rows directly (vocab tile 256, 128-column batch tiles); sampling,
-    greedy, logits store and the unfused path; same tokens as the tiled layout."""
+    """Row-major W with D a multiple of 256 above 64 rows: the row-major wide
+    kernel (vocab tile 256, 128-column batch tiles, 256-byte row runs through a
+    wave-private LDS transpose, rotated K order); sampling, greedy, logits
+    store and the unfused path; the tiled layout's tokens on every row the
+    oracle's margin decides (the two accumulate the K blocks in different
+    orders, so exact near-ties may differ)."""
     import torch
     D, V = 512, 2053
     H, W = _rand_head(B + 31, B, D, V)
@@ -451,7 +454,8 @@ def test_row_major_wide_kernel(fs, B):
     for T, seed, step in ((1.0, 0, 0), (0.6, 77, 2**32 + 1), (0.0, 0, 0)):
         tok = fs.sample_fused(Hd, Wd, T, seed, step).cpu().numpy()
         check_parity(H, W, T, seed, step, np.arange(B), tok)
-        assert np.array_equal(tok, fs.sample_fused(Hd, tw, T, seed, step).cpu().numpy())
+        firm = oracle.sample(H, W, T, seed, step).margin > TOL
+        assert np.array_equal(tok[firm], fs.sample_fused(Hd, tw, T, seed, step).cpu().numpy()[firm])
     l32 = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda")
     fs.sample_fused(Hd, Wd, 1.0, 0, 0, logits=l32)
     assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - oracle.exact_logits(H, W))) < 1e-4
