@@ -64,6 +64,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>) in order: a
+// loop whose index is a compile-time constant in its body, whatever the body's
+// size (register arrays indexed by it then stay in registers).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -700,12 +711,12 @@ constexpr int kWideRows = 16 * kWideNW * kWideMB;
 // the main loop no longer needs), then per batch row the tile's maximiser as
 // one key (and the tile's log-mass with MASS), published for Stage 2 or the
 // single-pass reduction.
-template <bool SAMPLE, bool STORE, bool MASS, int STAGE_BYTES>
-__device__ __forceinline__ void wide_epilogue(const Stage1Args& a, const f32x4 (&acc)[kWideMB][kWideNB],
-                                              const int (&m)[kWideMB], int vt, int b0, float* stage,
-                                              uint64_t (&red)[kWideNW][kWideBN],
-                                              float2 (&red_mass)[MASS ? kWideNW : 1][MASS ? kWideBN : 1]) {
-  constexpr int NB = kWideNB, NW = kWideNW, MB = kWideMB, BN = kWideBN, NT = 64 * NW;
+template <int NW, int MB, int NB, bool SAMPLE, bool STORE, bool MASS, int STAGE_BYTES>
+__device__ __forceinline__ void wide_epilogue(const Stage1Args& a, const f32x4 (&acc)[MB][NB], const int (&m)[MB],
+                                              int vt, int b0, float* stage, uint64_t (&red)[NW][16 * NB],
+                                              float2 (&red_mass)[MASS ? NW : 1][MASS ? 16 * NB : 1]) {
+  constexpr int BN = 16 * NB, NT = 64 * NW;
+  static_assert(NT >= BN, "one thread per batch column for the workgroup reduction");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -771,7 +782,7 @@ __device__ __forceinline__ void wide_epilogue(const Stage1Args& a, const f32x4 (
         }
       }
     };
-    const bool full = (int64_t)(vt + 1) * kWideRows <= a.V;
+    const bool full = (int64_t)(vt + 1) * (16 * NW * MB) <= a.V;
     if (a.greedy) {
       if (full) tile_max(std::true_type{}, std::true_type{});
       else tile_max(std::true_type{}, std::false_type{});
@@ -933,8 +944,8 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_wide_kernel(Stage1Args a, i
   for (int c = 0; c + 1 < nC; ++c) step(c, false);
   step(nC - 1, true);
 
-  wide_epilogue<SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, m, vt, b0, reinterpret_cast<float*>(lds_h4), red,
-                                                         red_mass);
+  wide_epilogue<NW, MB, NB, SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, m, vt, b0,
+                                                                     reinterpret_cast<float*>(lds_h4), red, red_mass);
 }
 
 // ------------------------------------------------------- MFMA, row-major W, wide tiles
@@ -1073,8 +1084,180 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_rows_wide_kernel(Stage1Args
     }
   }
 
-  wide_epilogue<SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, m, vt, b0, reinterpret_cast<float*>(lds_h4), red,
-                                                         red_mass);
+  wide_epilogue<NW, MB, NB, SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, m, vt, b0,
+                                                                     reinterpret_cast<float*>(lds_h4), red, red_mass);
+}
+
+// ------------------------------------------------------- MFMA, wide tiles, two workgroups per CU
+// Batches above 128 on the tiled layout (D a multiple of 256): the wide tile
+// of mfma_wide_kernel (8 waves x two 16-row blocks = 256 vocab rows, batch
+// tile 128, wave w owns row blocks vt * 16 + 8 j + w) in 128 registers, so
+// two workgroups share each CU and one's waits are covered by the other's
+// matrix work (measured: 6-12% faster at B = 384 .. 1024, up to 2% at
+// B = 129 .. 256; slower at one batch tile, where mfma_wide_kernel streams W
+// past the caches).
+//  * W: the A operands straight from the tiled layout, kRingPD K steps ahead
+//    (cached: the later batch tiles of a vocab tile run right after the first
+//    on one XCD and find W in its L2).
+//  * H: staged per 64-column sub-chunk in double-buffered LDS (160-byte
+//    rows), one barrier per sub-chunk. The B operands of a K step pass
+//    through a ring of kRingDepth registers instead of a full second set:
+//    each slot is refilled right after the matrix instructions that read it,
+//    the refills running on into the next K step (across the sub-chunk's
+//    barrier), so kRingDepth reads are always in flight.
+//  * Both operands are addressed from workgroup-uniform bases plus one 32-bit
+//    offset per lane, and the H loads are branch-free (rows past B read row
+//    B - 1, whose candidates are dropped; no column lies past D), so the
+//    compiler counts loads in flight instead of draining them and keeps
+//    few address registers.
+constexpr int kRingPD = 2;                     // W prefetch distance in K steps
+constexpr int kRingDepth = 4;                  // B-operand reads in flight
+constexpr int64_t kRingMaxLdh = int64_t(1) << 22;   // 32-bit H offsets within a batch tile
+
+template <bool SAMPLE, bool STORE, bool MASS>
+__global__ __launch_bounds__(64 * kWideNW, 2 * kWideNW / 4) void mfma_ring_kernel(Stage1Args a, int32_t n_bt) {
+  constexpr int NW = kWideNW, MB = kWideMB, NB = kWideNB, KSUB = kWideKSub, PD = kRingPD, R = kRingDepth;
+  constexpr int BN = kWideBN, NT = 64 * NW, KH = 32 * KSUB, ROW = KH + 16;   // 160-byte rows: conflict-free reads
+  constexpr int HP = BN * (KH / 8) / NT;       // 16-byte pieces of H per thread per sub-chunk
+  constexpr int NSUB = kKS / KSUB;
+  constexpr int kGroupsPerTile = NW * MB / kGroup;
+  static_assert(HP * NT == BN * (KH / 8), "H pieces per thread");
+  static_assert(kKS % PD == 0 && kKS % KSUB == 0 && NB % R == 0 && R <= NB, "pipeline shape");
+  static_assert(kGroup % NW == 0 && (NW * MB) % kGroup == 0, "row blocks of a tile fill whole groups");
+
+  __shared__ uint4 lds_h4[2 * BN * ROW / 8];
+  __shared__ uint64_t red[NW][BN];
+  __shared__ float2 red_mass[MASS ? NW : 1][MASS ? BN : 1];
+  uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
+
+  int vt, bt;
+  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int b0 = bt * BN;
+  const int D = a.D;
+  const int nC = (D + kBK - 1) / kBK;
+  const int nM = (a.V + 15) / 16;
+
+  // W: row block j of this wave sits in group mc / kGroup (0 or 1 within the
+  // tile), slot mc % kGroup; past V the last row block is read again
+  const char* w_wg = reinterpret_cast<const char*>(a.W) + (int64_t)vt * kGroupsPerTile * nC * kGroup * kBlock16 * 16;
+  int m[MB];
+  uint32_t woff[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    m[j] = vt * NW * MB + j * NW + wave;
+    const int mc = min(m[j], nM - 1);
+    const int g = mc / kGroup - vt * kGroupsPerTile;
+    woff[j] = (uint32_t)(((g * nC * kGroup + mc % kGroup) * kBlock16 + lane) * 16);
+  }
+  auto wpiece = [&](int j, int c, int t) {
+    const uint4* p =
+        reinterpret_cast<const uint4*>(w_wg + (woff[j] + (uint32_t)(c * kGroup * kBlock16 + t * 64) * 16u));
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  };
+
+  // H: piece i of this thread is row hn of the batch tile, columns hk .. +8
+  // of the sub-chunk
+  const char* h_wg = reinterpret_cast<const char*>(a.H) + (int64_t)b0 * a.ldh * 2;
+  uint32_t hrow[HP];
+  int hk[HP], hst[HP];
+#pragma unroll
+  for (int i = 0; i < HP; ++i) {
+    const int p = tid + NT * i;
+    const int hn = p / (KH / 8);
+    hk[i] = 8 * (p % (KH / 8));
+    hrow[i] = (uint32_t)min(hn, a.B - 1 - b0) * (uint32_t)a.ldh;
+    hst[i] = hn * ROW + hk[i];
+  }
+  auto load_h = [&](int s, uint4 (&h)[HP]) {   // sub-chunk s = columns s*KH .. +KH
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(h_wg + (hrow[i] + (uint32_t)(s * KH + hk[i])) * 2u);
+      h[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  };
+  auto store_h = [&](int buf, const uint4 (&h)[HP]) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4*>(lds_h + buf * BN * ROW + hst[i]) = h[i];
+  };
+  const uint16_t* lrd = lds_h + r * ROW + 8 * q;
+  auto read_b = [&](int buf, int tt, int nb) {
+    return *reinterpret_cast<const uint4*>(lrd + buf * BN * ROW + nb * 16 * ROW + 32 * tt);
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 w[MB][PD];
+  uint4 hreg[HP];
+  uint4 ring[R];
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int t = 0; t < PD; ++t) w[j][t] = wpiece(j, 0, t);
+  load_h(0, hreg);
+  store_h(0, hreg);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < R; ++i) ring[i] = read_b(0, 0, i);
+
+  // K block c. K step t uses W slot t % PD and refills it with step t + PD
+  // (in block c + 1 past the end of c; in the last block nothing is loaded
+  // past the end). The sub-chunk and step indices are compile-time
+  // constants (static_for), so every register array index is one.
+  auto step = [&](int c, bool last) {
+    static_for<NSUB>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
+      const int sidx = c * NSUB + s;
+      const int buf = sidx & 1;
+      const bool hmore = !last || s + 1 < NSUB;
+      if (hmore) load_h(sidx + 1, hreg);
+      static_for<KSUB>([&](auto tt_c) {
+        constexpr int tt = decltype(tt_c)::value;
+        constexpr int t = s * KSUB + tt;
+        constexpr int tn = t + PD;
+        const bool refill = !last || tn < kKS;
+        const int cn = tn < kKS ? c : c + 1;
+        constexpr bool in_sub = tt + 1 < KSUB;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int j = 0; j < MB; ++j) acc[j][nb] = mfma16x16x32(w[j][t % PD], ring[nb % R], acc[j][nb]);
+          const int nn = nb + R;
+          if (nn < NB) {
+            ring[nb % R] = read_b(buf, tt, nn);
+          } else if (in_sub) {
+            ring[nb % R] = read_b(buf, tt + 1, nn - NB);
+          } else if (hmore) {
+            if (nn == NB) {
+              store_h(buf ^ 1, hreg);
+              __syncthreads();
+            }
+            ring[nb % R] = read_b(buf ^ 1, 0, nn - NB);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // keep the ring order: R reads in flight, no more
+        }
+        if (refill) {
+#pragma unroll
+          for (int j = 0; j < MB; ++j) w[j][t % PD] = wpiece(j, cn, tn % kKS);
+        }
+      });
+    });
+  };
+  for (int c = 0; c + 1 < nC; ++c) step(c, false);
+  step(nC - 1, true);
+
+  wide_epilogue<NW, MB, NB, SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, m, vt, b0,
+                                                                     reinterpret_cast<float*>(lds_h4), red, red_mass);
 }
 
 // ------------------------------------------------------- MFMA, 256 x 256 tiles
@@ -1380,6 +1563,24 @@ hipError_t launch_rows_nw(const Stage1Args& a, hipStream_t stream) {
   return launch_rows_nb<4, NW>(a, stream);
 }
 
+hipError_t launch_mfma_ring(const Stage1Args& a, hipStream_t stream) {
+  const int n_bt = (a.B + kWideBN - 1) / kWideBN;
+  const bool sample = a.cand != nullptr;
+  const bool store = a.logits != nullptr;
+  const int64_t G = (int64_t)a.n_tiles * n_bt;
+  const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
+  if (a.ldh >= kRingMaxLdh || a.D % kBK != 0) return hipErrorInvalidValue;
+  void (*k)(Stage1Args, int32_t) = nullptr;
+  if (a.mass) k = store ? mfma_ring_kernel<true, true, true> : mfma_ring_kernel<true, false, true>;
+  else if (sample && store) k = mfma_ring_kernel<true, true, false>;
+  else if (sample) k = mfma_ring_kernel<true, false, false>;
+  else k = mfma_ring_kernel<false, true, false>;
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)G;
+  return launch(k, dim3((unsigned)grid), dim3(64 * kWideNW), 0, stream, b, (int32_t)n_bt);
+}
+
 template <bool ROWS, bool STREAMW>
 hipError_t launch_mfma_wide_k(const Stage1Args& a, int n_bt, hipStream_t stream) {
   const bool sample = a.cand != nullptr;
@@ -1427,6 +1628,8 @@ hipError_t launch_rows_wide(const Stage1Args& a, hipStream_t stream) {
 // step's).
 template <bool ROWS>
 hipError_t launch_mfma_wide(const Stage1Args& a, hipStream_t stream) {
+  // two or more batch tiles: the 128-register form, two workgroups per CU
+  if (!ROWS && a.B > kWideBN && a.D % kBK == 0 && a.ldh < kRingMaxLdh) return launch_mfma_ring(a, stream);
   const int n_bt = (a.B + kWideBN - 1) / kWideBN;
   if (!ROWS && n_bt <= 2) return launch_mfma_wide_k<false, true>(a, n_bt, stream);
   return launch_mfma_wide_k<ROWS, false>(a, n_bt, stream);

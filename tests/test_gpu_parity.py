@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from lm_head_gemm_amd import inputs
-from tests._util import TOL, check_parity, to_device
+from tests._util import TOL, check_grouped_parity, check_parity, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -237,6 +237,34 @@ def test_tiled_wide_store_and_unfused(fs, B):
             check_parity(H, W, 0.8, 6, 1, np.arange(B), tok)
         else:
             assert tok.min() >= 0 and tok.max() < V
+
+
+@pytest.mark.parametrize("B,D,V", [(129, 256, 999), (300, 512, 3001), (513, 1280, 2053), (1000, 768, 1234)])
+def test_tiled_wide_two_workgroups_per_cu(fs, B, D, V):
+    """The wide tile in 128 registers (two or more batch tiles on the tiled
+    layout with D a multiple of 256): ragged V and last batch tile, every row
+    against the oracle (sampling, another temperature and step, greedy),
+    single-pass equal to two-stage, stored logits exact to fp32 rounding, the
+    unfused baseline and the grouped variant's log-masses."""
+    import torch
+    H, W = _rand_head(B + 3 * D + V, B, D, V)
+    Hd = to_device(H)
+    tw = fs.TiledWeights(to_device(W))
+    assert fs.num_vocab_tiles(B, D, V, tiled=True) == (V + 255) // 256
+    rows = np.arange(B)
+    for T, seed, step in ((1.0, 3, 7), (0.6, 77, 2**32 + 1), (0.0, 0, 0)):
+        tok = fs.sample_fused(Hd, tw, T, seed, step).cpu().numpy()
+        check_parity(H, W, T, seed, step, rows, tok)
+        assert np.array_equal(tok, fs.sample_fused(Hd, tw, T, seed, step, single_pass=True).cpu().numpy())
+    exact = oracle.exact_logits(H, W)
+    l32 = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda")
+    tok = fs.sample_fused(Hd, tw, 1.0, 4, 4, logits=l32).cpu().numpy()
+    assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - exact)) < 1e-4
+    check_parity(H, W, 1.0, 4, 4, rows, tok)
+    tok = fs.sample_unfused(Hd, tw, 0.8, 6, 1, logits_dtype=torch.float32).cpu().numpy()
+    check_parity(H, W, 0.8, 6, 1, rows, tok)
+    tok = fs.sample_fused(Hd, tw, 0.9, 1, 2, group_size=512).cpu().numpy()
+    check_grouped_parity(H, W, 0.9, 1, 2, 512, rows, tok)
 
 
 @pytest.mark.parametrize("layout,variant,dtype", [
