@@ -32,13 +32,19 @@ struct Key2 {
   uint32_t k0, k1;
 };
 
+// a ^ b ^ c in one gfx950 instruction (v_bitop3_b32 with the truth table of
+// three-input parity, 0x96)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)kPhiloxM0 * c.x;
     const uint64_t p1 = (uint64_t)kPhiloxM1 * c.z;
-    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
-                   (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    c = make_uint4(xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1,
+                   xor3((uint32_t)(p0 >> 32), c.w, k1), (uint32_t)p0);
     k0 += kPhiloxW0;
     k1 += kPhiloxW1;
   }
@@ -82,12 +88,12 @@ constexpr float kNegLnLn2 = 0.366512920581664327f;   // -ln(ln 2)
 
 __device__ __forceinline__ float gumbel2_from_word(uint32_t x) {
   const bool low = x < 0x80000000u;
-  const float u = fmaf((float)x, 0x1p-32f, 0x1p-33f);
-  const float c = fmaf((float)(~x), 0x1p-32f, 0x1p-33f);
-  const float w = 1.0f - c;
-  const float d = (1.0f - w) - c;
+  // one conversion: v = u for x < 2^31, else v = c = 1 - u (from ~x)
+  const float v = fmaf((float)(low ? x : ~x), 0x1p-32f, 0x1p-33f);
+  const float w = 1.0f - v;
+  const float d = (1.0f - w) - v;
   const float corr = low ? 0.0f : d * (2.0f - w);          // ln(1 - c) - ln w
-  const float e2 = fmaf(corr, -kInvLn2, -__builtin_amdgcn_logf(low ? u : w));
+  const float e2 = fmaf(corr, -kInvLn2, -__builtin_amdgcn_logf(low ? v : w));
   return -__builtin_amdgcn_logf(e2);
 }
 
