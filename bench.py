@@ -333,13 +333,39 @@ def traffic_record(kernel: str, workload: str, B: int):
     return r.get("bytes_per_launch")
 
 
-def sweep_workload(fs, wl, steps, repeats, warm_ms, vendor=True):
+def oracle_timings(wl, H, W):
+    """The CPU oracle, end to end (widening, fp64 logits, Philox, Gumbel,
+    top-2), on one decode step of this workload at its smallest and largest
+    batch with the host's BLAS threads, and on one thread at B = 1 for the two
+    smallest heads. Returns a list of dicts."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    cases = sorted({(min(wl.batches), 0), (max(wl.batches), 0)})
+    if wl.name in ("tiny_f32", "llama3_8b"):
+        cases.append((1, 1))
+    out = []
+    for B, threads in cases:
+        t0 = time.perf_counter()
+        if threads:
+            with threadpool_limits(limits=threads):
+                oracle.sample(H[:B], W, wl.temperature, wl.seed, 0)
+        else:
+            oracle.sample(H[:B], W, wl.temperature, wl.seed, 0)
+        sec = time.perf_counter() - t0
+        out.append({"workload": wl.name, "B": B, "seconds": round(sec, 3), "samples_per_s": round(B / sec, 2),
+                    "threads": threads or "blas default"})
+        log(f"[bench] oracle {wl.name} B={B} ({out[-1]['threads']} threads): {sec:.2f} s")
+    return out
+
+
+def sweep_workload(fs, wl, steps, repeats, warm_ms, vendor=True, cpu=None):
     """Compact sweep entries for every B of one workload: the fused call on
     the layout the headline uses (tiled for bf16 heads, row-major for fp32),
     its Stage-1 HBM and matrix-core fractions, and beside it the plain call on
     row-major W, single-pass (B <= 8), the unfused baseline (bf16 logits), the
     store-logits option (IO-model check) and, for bf16 heads, the library GEMM
-    alone. Returns a list of dicts."""
+    alone. Returns a list of dicts; with a list as `cpu`, the CPU oracle's
+    timings of this workload are appended to it."""
     import torch
     from lm_head_gemm_amd import inputs
     t = time.perf_counter()
@@ -347,6 +373,8 @@ def sweep_workload(fs, wl, steps, repeats, warm_ms, vendor=True):
     W = inputs.make_weights(wl)
     Hd = upload(H)
     Wr = [upload(W), upload(W)]
+    if cpu is not None:
+        cpu += oracle_timings(wl, H, W)
     del H, W
     tiled = wl.dtype == "bf16"
     Wt = [fs.TiledWeights(w) for w in Wr] if tiled else Wr
@@ -633,11 +661,14 @@ def main():
         Ws_rows = vendor_rows = None
         torch.cuda.empty_cache()
         entries = []
+        cpu = None if args.no_cpu_baseline else []
         for name in [x for x in args.sweep_workloads.split(",") if x]:
             entries += sweep_workload(fs, inputs.WORKLOADS[name], args.sweep_steps, args.sweep_repeats,
-                                      min(args.min_warmup_ms, 100.0), vendor=not args.no_vendor)
+                                      min(args.min_warmup_ms, 100.0), vendor=not args.no_vendor, cpu=cpu)
         result["sweep"] = {"steps": args.sweep_steps, "repeats": args.sweep_repeats,
                            "layout": "tiled for bf16 heads, row-major for fp32", "entries": entries}
+        if cpu:
+            result["sweep"]["oracle_cpu"] = cpu
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(H, W, wl, B)
