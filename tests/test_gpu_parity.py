@@ -267,6 +267,25 @@ def test_tiled_wide_two_workgroups_per_cu(fs, B, D, V):
     check_grouped_parity(H, W, 0.9, 1, 2, 512, rows, tok)
 
 
+def test_wide_tile_huge_h_stride(fs):
+    """H rows 2^22 + 256 elements apart (past the 32-bit offsets of the
+    two-workgroup wide tile, which then hands the call to the one-workgroup
+    wide kernel): every row against the oracle, the same tokens as with a
+    contiguous H."""
+    import torch
+    B, D, V = 130, 256, 999
+    H, W = _rand_head(77, B, D, V)
+    big = torch.zeros((B, (1 << 22) + 256), dtype=torch.bfloat16, device="cuda")
+    big[:, 128:128 + D] = to_device(H)
+    Hs = big[:, 128:128 + D]
+    assert Hs.stride(0) == (1 << 22) + 256
+    tw = fs.TiledWeights(to_device(W))
+    tok = fs.sample_fused(Hs, tw, 1.0, 5, 6).cpu().numpy()
+    check_parity(H, W, 1.0, 5, 6, np.arange(B), tok)
+    assert np.array_equal(tok, fs.sample_fused(to_device(H), tw, 1.0, 5, 6).cpu().numpy())
+    del big
+
+
 @pytest.mark.parametrize("layout,variant,dtype", [
     ("rows", "gemv", "bf16"), ("rows", "mfma", "bf16"), ("rows", "gemv", "f32"), ("rows", "mfma", "f32"),
     ("tiled", "gemv", "bf16"), ("tiled", "mfma", "bf16"),
