@@ -37,6 +37,7 @@
 // a running maximum per batch row, one candidate key per (row, vocab tile);
 // optionally the tile's log-mass (grouped variant) and the logits (stored
 // through LDS as whole row segments).
+#include <atomic>
 #include <type_traits>
 
 #include "fs_common.h"
@@ -1088,14 +1089,20 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_rows_wide_kernel(Stage1Args
                                                                      reinterpret_cast<float*>(lds_h4), red, red_mass);
 }
 
-// ------------------------------------------------------- MFMA, wide tiles, two workgroups per CU
+// ------------------------------------------------------- MFMA, wide tiles in few registers
 // Batches above 128 on the tiled layout (D a multiple of 256): the wide tile
-// of mfma_wide_kernel (8 waves x two 16-row blocks = 256 vocab rows, batch
-// tile 128, wave w owns row blocks vt * 16 + 8 j + w) in 128 registers, so
-// two workgroups share each CU and one's waits are covered by the other's
-// matrix work (measured: 6-12% faster at B = 384 .. 1024, up to 2% at
-// B = 129 .. 256; slower at one batch tile, where mfma_wide_kernel streams W
-// past the caches).
+// of mfma_wide_kernel (8 waves x two 16-row blocks = 256 vocab rows, wave w
+// owns row blocks vt * 16 + 8 j + w) with NB 16-column batch blocks:
+//  * NB = 8 (batch tile 128) in 128 registers, so two workgroups share each
+//    CU and one's waits are covered by the other's matrix work (measured:
+//    6-12% faster than mfma_wide_kernel at B = 384 .. 1024, up to 2% at
+//    B = 129 .. 256; slower at one batch tile, where mfma_wide_kernel streams
+//    W past the caches);
+//  * NB = 16 (batch tile 256) in 242 registers, one workgroup per CU: for
+//    B = 129 .. 256 W is streamed once instead of once per 128 columns
+//    (measured: 2-5% faster than NB = 8 when the last round of workgroups is
+//    nearly full, 10% slower when it is a third full, as with 594 tiles on
+//    256 CUs: the launcher checks).
 //  * W: the A operands straight from the tiled layout, kRingPD K steps ahead
 //    (cached: the later batch tiles of a vocab tile run right after the first
 //    on one XCD and find W in its L2).
@@ -1113,11 +1120,13 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_rows_wide_kernel(Stage1Args
 constexpr int kRingPD = 2;                     // W prefetch distance in K steps
 constexpr int kRingDepth = 4;                  // B-operand reads in flight
 constexpr int64_t kRingMaxLdh = int64_t(1) << 22;   // 32-bit H offsets within a batch tile
+constexpr int kRingWideNB = 16;                // column blocks of the one-workgroup-per-CU form
 
-template <bool SAMPLE, bool STORE, bool MASS>
-__global__ __launch_bounds__(64 * kWideNW, 2 * kWideNW / 4) void mfma_ring_kernel(Stage1Args a, int32_t n_bt) {
-  constexpr int NW = kWideNW, MB = kWideMB, NB = kWideNB, KSUB = kWideKSub, PD = kRingPD, R = kRingDepth;
-  constexpr int BN = kWideBN, NT = 64 * NW, KH = 32 * KSUB, ROW = KH + 16;   // 160-byte rows: conflict-free reads
+template <int NB, bool SAMPLE, bool STORE, bool MASS>
+__global__ __launch_bounds__(64 * kWideNW, (NB == kWideNB ? 2 : 1) * kWideNW / 4) void mfma_ring_kernel(Stage1Args a,
+                                                                                                    int32_t n_bt) {
+  constexpr int NW = kWideNW, MB = kWideMB, KSUB = kWideKSub, PD = kRingPD, R = kRingDepth;
+  constexpr int BN = 16 * NB, NT = 64 * NW, KH = 32 * KSUB, ROW = KH + 16;   // 160-byte rows: conflict-free reads
   constexpr int HP = BN * (KH / 8) / NT;       // 16-byte pieces of H per thread per sub-chunk
   constexpr int NSUB = kKS / KSUB;
   constexpr int kGroupsPerTile = NW * MB / kGroup;
@@ -1563,8 +1572,9 @@ hipError_t launch_rows_nw(const Stage1Args& a, hipStream_t stream) {
   return launch_rows_nb<4, NW>(a, stream);
 }
 
-hipError_t launch_mfma_ring(const Stage1Args& a, hipStream_t stream) {
-  const int n_bt = (a.B + kWideBN - 1) / kWideBN;
+template <int NB>
+hipError_t launch_mfma_ring_k(const Stage1Args& a, hipStream_t stream) {
+  const int n_bt = (a.B + 16 * NB - 1) / (16 * NB);
   const bool sample = a.cand != nullptr;
   const bool store = a.logits != nullptr;
   const int64_t G = (int64_t)a.n_tiles * n_bt;
@@ -1572,13 +1582,37 @@ hipError_t launch_mfma_ring(const Stage1Args& a, hipStream_t stream) {
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
   if (a.ldh >= kRingMaxLdh || a.D % kBK != 0) return hipErrorInvalidValue;
   void (*k)(Stage1Args, int32_t) = nullptr;
-  if (a.mass) k = store ? mfma_ring_kernel<true, true, true> : mfma_ring_kernel<true, false, true>;
-  else if (sample && store) k = mfma_ring_kernel<true, true, false>;
-  else if (sample) k = mfma_ring_kernel<true, false, false>;
-  else k = mfma_ring_kernel<false, true, false>;
+  if (a.mass) k = store ? mfma_ring_kernel<NB, true, true, true> : mfma_ring_kernel<NB, true, false, true>;
+  else if (sample && store) k = mfma_ring_kernel<NB, true, true, false>;
+  else if (sample) k = mfma_ring_kernel<NB, true, false, false>;
+  else k = mfma_ring_kernel<NB, false, true, false>;
   Stage1Args b = a;
   b.total_wgs = (int32_t)G;
   return launch(k, dim3((unsigned)grid), dim3(64 * kWideNW), 0, stream, b, (int32_t)n_bt);
+}
+
+// Compute units of the current device (queried once per device; 0 if the
+// query fails).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    cache[dev].store(n, std::memory_order_relaxed);
+  return n > 0 ? n : 0;
+}
+
+// One 256-column batch tile (one workgroup per CU) when it covers B and the
+// last round of workgroups is empty or at least three quarters full; else
+// 128-column batch tiles at two workgroups per CU.
+hipError_t launch_mfma_ring(const Stage1Args& a, hipStream_t stream) {
+  if (a.B <= 16 * kRingWideNB) {
+    const int cus = device_cu_count();
+    const int64_t rem = cus > 0 ? a.n_tiles % cus : -1;
+    if (rem == 0 || 4 * rem >= 3 * (int64_t)cus) return launch_mfma_ring_k<kRingWideNB>(a, stream);
+  }
+  return launch_mfma_ring_k<kWideNB>(a, stream);
 }
 
 template <bool ROWS, bool STREAMW>

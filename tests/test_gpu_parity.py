@@ -267,6 +267,34 @@ def test_tiled_wide_two_workgroups_per_cu(fs, B, D, V):
     check_grouped_parity(H, W, 0.9, 1, 2, 512, rows, tok)
 
 
+def test_tiled_wide_one_batch_tile_of_256(fs):
+    """B = 129 .. 256 on vocabularies whose 256-row tiles fill the last round
+    of one-per-CU workgroups completely or to seven eighths (the 256-column
+    form of the wide tile): every row against the oracle, greedy, single-pass,
+    stored logits, the unfused baseline and the grouped variant."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, D, V in [(200, 256, cus * 256 - 7), (256, 512, (cus + 7 * cus // 8) * 256 - 100),
+                    (129, 768, (2 * cus) * 256 - 255)]:
+        H, W = _rand_head(B + D + V, B, D, V)
+        Hd = to_device(H)
+        tw = fs.TiledWeights(to_device(W))
+        rows = np.arange(B)
+        for T, seed, step in ((1.0, 8, 3), (0.0, 0, 0)):
+            tok = fs.sample_fused(Hd, tw, T, seed, step).cpu().numpy()
+            check_parity(H, W, T, seed, step, rows, tok)
+            assert np.array_equal(tok, fs.sample_fused(Hd, tw, T, seed, step, single_pass=True).cpu().numpy())
+        l32 = torch.full((B, V), float("nan"), dtype=torch.float32, device="cuda")
+        tok = fs.sample_fused(Hd, tw, 1.0, 4, 4, logits=l32).cpu().numpy()
+        assert np.max(np.abs(l32.cpu().numpy().astype(np.float64) - oracle.exact_logits(H, W))) < 1e-4
+        check_parity(H, W, 1.0, 4, 4, rows, tok)
+        del l32
+        tok = fs.sample_unfused(Hd, tw, 0.8, 6, 1, logits_dtype=torch.float32).cpu().numpy()
+        check_parity(H, W, 0.8, 6, 1, rows, tok)
+        tok = fs.sample_fused(Hd, tw, 0.9, 1, 2, group_size=4096).cpu().numpy()
+        check_grouped_parity(H, W, 0.9, 1, 2, 4096, rows, tok)
+
+
 def test_wide_tile_huge_h_stride(fs):
     """H rows 2^22 + 256 elements apart (past the 32-bit offsets of the
     two-workgroup wide tile, which then hands the call to the one-workgroup
