@@ -18,15 +18,21 @@
 // streams 32 or 64 KiB of contiguous memory: the access pattern HBM serves
 // best (measured: 86% of peak, against 75% for 16-row interleaved reads).
 //
-// Three kernels read it:
+// Four kernels read it:
 //  * GEMV (B <= 2): each lane accumulates bf16 dot products of its row piece
 //    with H (staged once in LDS; the four lanes of a row share nothing but
 //    the reduction), then two butterfly steps finish each row's sum;
 //  * MFMA (B up to 64): the A operand comes straight from the loads; H
 //    chunks are staged in LDS and shared by the workgroup's waves, one row
 //    block per wave;
-//  * wide MFMA (B > 64): two row blocks per wave and 128-column batch tiles,
-//    H staged in sub-chunks and the B operands read one K step ahead.
+//  * wide MFMA (B 65 .. 128, and above when D is not a multiple of 256): two
+//    row blocks per wave and 128-column batch tiles, H staged in sub-chunks
+//    and the B operands read one K step ahead;
+//  * the wide tile in few registers (B > 128, D a multiple of 256): the B
+//    operands through a short register ring, so that two workgroups share a
+//    CU (128-column batch tiles) or one 256-column batch tile fits.
+// (An opt-in 256 x 256 tile with both operands copied into LDS exists for
+// measurement; it is never chosen by itself.)
 // Row-major W whose D is a multiple of 256 is read by three more kernels:
 // mfma_rows_kernel (B up to 64) and mfma_rows_wide_kernel (B up to 128), with
 // 256-byte row runs per wave load moved to operand order through a
