@@ -581,12 +581,13 @@ def test_concurrent_streams_with_distinct_workspaces(fs):
 
 
 @pytest.mark.parametrize("single_pass", [False, True])
-def test_graph_capture_and_replay(fs, single_pass):
+@pytest.mark.parametrize("B,D,V", [(24, 1024, 2053), (300, 512, 3001)])
+def test_graph_capture_and_replay(fs, single_pass, B, D, V):
     """A fused call enqueues only kernel launches, so it can be captured in a
     HIP graph: every replay (with new hidden states copied into the captured
-    input between replays, and eager calls in between) equals the eager call."""
+    input between replays, and eager calls in between) equals the eager call.
+    Narrow tile (24 rows) and the register-ring wide tile (300 rows)."""
     import torch
-    B, D, V = 24, 1024, 2053
     H, W = _rand_head(43, B, D, V)
     Hd = to_device(H)
     tw = fs.TiledWeights(to_device(W))
