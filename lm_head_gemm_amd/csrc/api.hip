@@ -87,9 +87,9 @@ struct FusedCall {
 //     rows and the wide kernel (256 rows) from 65 on; other D the
 //     LDS-transposing kernel (64 or 128 rows); fp32 the fp32 matrix-core
 //     kernel (128 rows).
-//   Tiled W (bf16): the same split; vocab tile 64 or 128 rows (4 or 8 waves
-//     of one 16-row block each), and for MFMA batches from 65 rows on the
-//     256-row wide tile (8 waves of two blocks, batch tile 128).
+//   Tiled W (bf16): MFMA at every B (GEMV when asked for); vocab tile 64 or
+//     128 rows (4 or 8 waves of one 16-row block each), and from 65 rows on
+//     the 256-row wide tile (8 waves of two blocks, batch tile 128 or 256).
 //   group_size > 0 (grouped variant): the MFMA kernels with the log-mass
 //     epilogue; groups must be unions of vocab tiles.
 bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* o, Plan* p,
@@ -133,7 +133,10 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
     return true;
   }
   const bool long_rows = layout == FS_LAYOUT_ROWS && dtype == FS_DTYPE_BF16 && D >= kGemvLongRowD;
-  if (variant == FS_VARIANT_AUTO) variant = B > kGemvMaxB ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
+  // tiled W: the matrix-core kernels at every B (measured 0-2.3% faster than
+  // GEMV at B <= 2: the 128-row tiles stream the layout's 64 KiB runs)
+  if (variant == FS_VARIANT_AUTO)
+    variant = (B > kGemvMaxB || layout == FS_LAYOUT_TILED) ? FS_VARIANT_MFMA : FS_VARIANT_GEMV;
   if (variant == FS_VARIANT_MFMA && dtype == FS_DTYPE_F32 && layout == FS_LAYOUT_ROWS) {
     // fp32 matrix-core kernel: 128-row vocab tiles, batch tiles of 16, 32 or 64
     if (tile == 0) tile = mfma_f32_tile_rows();
