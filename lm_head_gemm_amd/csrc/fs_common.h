@@ -257,6 +257,7 @@ struct Stage1Args {
   uint64_t* keys;       // [B] running maximum keys, zero between calls
   uint32_t* counter;    // finished-workgroup counters (kSpGroups + 1 slots), zero between calls
   int32_t* out;         // [B] tokens
+  int32_t split_tiles;  // the last split_tiles vocab tiles run as two half batch tiles (set by the launcher)
 };
 
 // Stores l[0..3], the logits of batch row b at vocab rows v0 .. v0+3 (those
@@ -312,6 +313,15 @@ __device__ __forceinline__ bool tile_of(int L, int n_vt, int n_bt, int* vt, int*
   return true;
 }
 
+// Launch index i (counted from the first split slot) -> (vocab tile, batch
+// half) of the split tiles: the two halves of a tile are kXcds slots apart,
+// so they run on one XCD. Returns false for padding slots.
+__device__ __forceinline__ bool split_tile_of(int i, int n_split, int* vt, int* half) {
+  *vt = i / (2 * kXcds) * kXcds + i % kXcds;
+  *half = (i / kXcds) & 1;
+  return *vt < n_split;
+}
+
 // Single-pass bookkeeping in the workspace after the [B] keys: one counter
 // per group of vocab tiles (tile mod kSpGroups) and one for the groups, each
 // in its own 256-byte slot (uint32 index kSpSlot * slot).
@@ -355,10 +365,14 @@ __device__ __forceinline__ void publish_candidates(const Stage1Args& a, int tile
   __builtin_amdgcn_s_waitcnt(0);  // the maxima have been performed
   __syncthreads();
   if (tid == 0) {
-    // workgroups per group: the group's vocab tiles times the batch tiles
+    // workgroups per group: the group's vocab tiles times the batch tiles,
+    // its split tiles (the last a.split_tiles, one batch tile) counted twice
     const int g = tile % kSpGroups;
-    const int n_bt = a.total_wgs / a.n_tiles;
-    const uint32_t in_group = (uint32_t)(((a.n_tiles - g + kSpGroups - 1) / kSpGroups) * n_bt);
+    const int whole = a.n_tiles - a.split_tiles;
+    const int n_bt = a.split_tiles ? 1 : a.total_wgs / a.n_tiles;
+    const int tiles = (a.n_tiles - g + kSpGroups - 1) / kSpGroups;
+    const int whole_tiles = whole > g ? (whole - g + kSpGroups - 1) / kSpGroups : 0;
+    const uint32_t in_group = (uint32_t)(whole_tiles * n_bt + 2 * (tiles - whole_tiles));
     const uint32_t groups = (uint32_t)min(a.n_tiles, kSpGroups);
     int last = 0;
     if (__hip_atomic_fetch_add(a.counter + kSpSlot * g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==

@@ -383,7 +383,16 @@ __device__ __forceinline__ uint4 lane_gather(const uint4& v, int addr) {
                     (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w));
 }
 
-template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false>
+// With SPLIT, a launch covers only the last a.split_tiles vocab tiles, each
+// as two workgroups (one per 16 NB-column half of a batch tile twice as wide,
+// n_bt unused); the launch of the other tiles is the one without SPLIT. Where
+// the last round of workgroups would be at most a quarter full, twice as many
+// workgroups with half the matrix and epilogue work each finish it sooner
+// (measured on 4096-wide heads at B = 24 and 64: 12% faster with the last
+// round 6-20% full, slower from about a third). The two halves of a tile read
+// the same W with cached loads and run on one XCD, so the second read is
+// mostly served by its L2; whole tiles stream W past it.
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false, bool SPLIT = false>
 __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
   constexpr int BN = 16 * NB;
   constexpr int NT = 64 * NW;
@@ -396,7 +405,12 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
 
   int vt, bt;
-  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+  if constexpr (SPLIT) {
+    if (!split_tile_of(blockIdx.x, a.split_tiles, &vt, &bt)) return;  // whole workgroup
+    vt += a.n_tiles - a.split_tiles;
+  } else if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) {
+    return;  // whole workgroup
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -413,7 +427,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   constexpr int kTStride = 64;
   const uint4* wt = static_cast<const uint4*>(a.W) + lane;
   auto wblock = [&](int c) { return wt + block_piece(mc, c, nC); };
-  auto wload = [&](const uint4* p) { return load_stream16(p); };   // read once: non-temporal
+  auto wload = [&](const uint4* p) { return SPLIT ? *p : load_stream16(p); };   // else read once: non-temporal
   const uint16_t* H = static_cast<const uint16_t*>(a.H);
 
   // This thread's share of each H block: rows hn[i], columns hk[i] .. +8;
@@ -1530,24 +1544,73 @@ hipError_t launch_gemv_nw(const Stage1Args& a, hipStream_t stream) {
   return launch_gemv_bb<4, NW>(a, stream);
 }
 
-template <int NB, int NW>
-hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
+int device_cu_count();
+
+// Workgroups of kernel K (`threads` per workgroup, static LDS only) resident
+// at once on the current device: queried once per device, 0 if unknown.
+template <auto K>
+int resident_wgs(int threads) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(K), threads, 0) !=
+            hipSuccess ||
+        per_cu <= 0)
+      return 0;
+    n = per_cu * device_cu_count();
+    if (n > 0) cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Vocab tiles to split in two (see mfma_tiled_kernel): those of a last round
+// that would be at most a quarter full, when a full round comes before it.
+int64_t ragged_split(int64_t n_tiles, int64_t slots) {
+  if (slots <= 0 || n_tiles <= slots) return 0;
+  const int64_t rem = n_tiles % slots;
+  return 4 * rem <= slots ? rem : 0;
+}
+
+// The whole tiles, then (when the last round is split) the split tiles as
+// half-width batch tiles in a second launch on the same stream.
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS>
+hipError_t launch_mfma_nb_k(const Stage1Args& a, hipStream_t stream) {
   constexpr int BN = 16 * NB;
-  const bool sample = a.cand != nullptr;
-  const bool store = a.logits != nullptr;
+  constexpr auto k = mfma_tiled_kernel<NB, NW, SAMPLE, STORE, MASS>;
   const int n_bt = (a.B + BN - 1) / BN;
-  const int64_t G = (int64_t)a.n_tiles * n_bt;
+  Stage1Args b = a;
+  b.split_tiles = 0;
+  // both halves of a split tile hold batch rows
+  if (NB % 2 == 0 && n_bt == 1 && a.B > BN / 2)
+    b.split_tiles = (int32_t)ragged_split(a.n_tiles, resident_wgs<k>(64 * NW));
+  const int64_t G = (int64_t)(a.n_tiles - b.split_tiles) * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
-  void (*k)(Stage1Args, int32_t) = nullptr;
+  b.total_wgs = (int32_t)(G + 2 * (int64_t)b.split_tiles);
+  hipError_t e = launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b, (int32_t)n_bt);
+  if constexpr (NB % 2 == 0) {
+    if (e == hipSuccess && b.split_tiles > 0) {
+      const int64_t halves = (2 * (int64_t)b.split_tiles + 2 * kXcds - 1) / (2 * kXcds) * (2 * kXcds);
+      e = launch(mfma_tiled_kernel<NB / 2, NW, SAMPLE, STORE, MASS, true>, dim3((unsigned)halves), dim3(64 * NW), 0,
+                 stream, b, (int32_t)1);
+    }
+  }
+  return e;
+}
+
+template <int NB, int NW>
+hipError_t launch_mfma_nb(const Stage1Args& a, hipStream_t stream) {
+  const bool sample = a.cand != nullptr;
+  const bool store = a.logits != nullptr;
   if (a.mass)
-    k = store ? mfma_tiled_kernel<NB, NW, true, true, true> : mfma_tiled_kernel<NB, NW, true, false, true>;
-  else if (sample && store) k = mfma_tiled_kernel<NB, NW, true, true, false>;
-  else if (sample) k = mfma_tiled_kernel<NB, NW, true, false, false>;
-  else k = mfma_tiled_kernel<NB, NW, false, true, false>;
-  Stage1Args b = a;
-  b.total_wgs = (int32_t)G;
-  return launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b, (int32_t)n_bt);
+    return store ? launch_mfma_nb_k<NB, NW, true, true, true>(a, stream)
+                 : launch_mfma_nb_k<NB, NW, true, false, true>(a, stream);
+  if (sample && store) return launch_mfma_nb_k<NB, NW, true, true, false>(a, stream);
+  if (sample) return launch_mfma_nb_k<NB, NW, true, false, false>(a, stream);
+  return launch_mfma_nb_k<NB, NW, false, true, false>(a, stream);
 }
 
 template <int NB, int NW>

@@ -295,6 +295,34 @@ def test_tiled_wide_one_batch_tile_of_256(fs):
         check_grouped_parity(H, W, 0.9, 1, 2, 4096, rows, tok)
 
 
+def test_tiled_ragged_last_round_split(fs):
+    """B = 17 .. 64 on vocabularies whose 128-row tiles leave the last round of
+    two-per-CU workgroups at most half full (those tiles then run as two
+    half-width batch tiles each): every row against the oracle, greedy,
+    single-pass (whose finish counts take the split tiles twice), the grouped
+    variant, and stored logits (a path without the split)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, D, V in [(64, 256, (2 * cus + cus // 3) * 128 + 5), (40, 512, (4 * cus + 1) * 128),
+                    (24, 256, (2 * cus + cus // 2) * 128 - 3)]:
+        H, W = _rand_head(B + D + V, B, D, V)
+        Hd = to_device(H)
+        tw = fs.TiledWeights(to_device(W))
+        rows = np.arange(B)
+        for T, seed, step in ((1.0, 5, 2), (0.0, 0, 0)):
+            tok = fs.sample_fused(Hd, tw, T, seed, step).cpu().numpy()
+            check_parity(H, W, T, seed, step, rows, tok)
+            for _ in range(2):   # the second call finds the single-pass counters returned to zero
+                assert np.array_equal(tok, fs.sample_fused(Hd, tw, T, seed, step, single_pass=True).cpu().numpy())
+        tok = fs.sample_fused(Hd, tw, 0.9, 1, 2, group_size=4096).cpu().numpy()
+        check_grouped_parity(H, W, 0.9, 1, 2, 4096, rows, tok)
+        l16 = torch.empty((B, V), dtype=torch.bfloat16, device="cuda")
+        tok = fs.sample_fused(Hd, tw, 1.0, 5, 2, logits=l16).cpu().numpy()
+        check_parity(H, W, 1.0, 5, 2, rows, tok)
+        assert_bf16_logits(l16.float().cpu().numpy().astype(np.float64), oracle.exact_logits(H, W))
+        del l16
+
+
 def test_wide_tile_huge_h_stride(fs):
     """H rows 2^22 + 256 elements apart (past the 32-bit offsets of the
     two-workgroup wide tile, which then hands the call to the one-workgroup
