@@ -615,6 +615,19 @@ def test_graph_capture_and_replay(fs, single_pass, B, D, V):
     HIP graph: every replay (with new hidden states copied into the captured
     input between replays, and eager calls in between) equals the eager call.
     Narrow tile (24 rows) and the register-ring wide tile (300 rows)."""
+    _graph_capture_check(fs, single_pass, B, D, V)
+
+
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_graph_capture_split_last_round(fs, single_pass):
+    """The same with a nearly empty last round of 128-row tiles, which the
+    launcher runs as a second launch of half-width batch tiles."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _graph_capture_check(fs, single_pass, 64, 256, (2 * cus + cus // 5) * 128 + 9)
+
+
+def _graph_capture_check(fs, single_pass, B, D, V):
     import torch
     H, W = _rand_head(43, B, D, V)
     Hd = to_device(H)
