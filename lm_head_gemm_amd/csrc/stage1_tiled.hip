@@ -1130,14 +1130,14 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_rows_wide_kernel(Stage1Args
 //    6-12% faster than mfma_wide_kernel at B = 384 .. 1024, up to 2% at
 //    B = 129 .. 256; slower at one batch tile, where mfma_wide_kernel streams
 //    W past the caches);
-//  * NB = 16 (batch tile 256) in 242 registers, one workgroup per CU: for
+//  * NB = 16 (batch tile 256) in 246 registers, one workgroup per CU: for
 //    B = 129 .. 256 W is streamed once instead of once per 128 columns
 //    (measured: 2-5% faster than NB = 8 when the last round of workgroups is
 //    nearly full, 10% slower when it is a third full, as with 594 tiles on
 //    256 CUs: the launcher checks).
-//  * W: the A operands straight from the tiled layout, kRingPD K steps ahead
-//    (cached: the later batch tiles of a vocab tile run right after the first
-//    on one XCD and find W in its L2).
+//  * W: the A operands straight from the tiled layout, ring_pd(NB) K steps
+//    ahead (cached: the later batch tiles of a vocab tile run right after the
+//    first on one XCD and find W in its L2).
 //  * H: staged per 64-column sub-chunk in double-buffered LDS (160-byte
 //    rows), one barrier per sub-chunk. The B operands of a K step pass
 //    through a ring of kRingDepth registers instead of a full second set:
@@ -1149,15 +1149,19 @@ __global__ __launch_bounds__(64 * kWideNW) void mfma_rows_wide_kernel(Stage1Args
 //    B - 1, whose candidates are dropped; no column lies past D), so the
 //    compiler counts loads in flight instead of draining them and keeps
 //    few address registers.
-constexpr int kRingPD = 2;                     // W prefetch distance in K steps
 constexpr int kRingDepth = 4;                  // B-operand reads in flight
 constexpr int64_t kRingMaxLdh = int64_t(1) << 22;   // 32-bit H offsets within a batch tile
 constexpr int kRingWideNB = 16;                // column blocks of the one-workgroup-per-CU form
+// W prefetch distance in K steps: 2 in the 128-register form; 4 with 16
+// column blocks, whose two waves per SIMD hide less latency (4 more
+// registers, 246; measured 0.5-3% faster at B = 129-256 on the 4096-, 7168-
+// and 8192-wide heads)
+constexpr int ring_pd(int NB) { return NB == kRingWideNB ? 4 : 2; }
 
 template <int NB, bool SAMPLE, bool STORE, bool MASS>
 __global__ __launch_bounds__(64 * kWideNW, (NB == kWideNB ? 2 : 1) * kWideNW / 4) void mfma_ring_kernel(Stage1Args a,
                                                                                                     int32_t n_bt) {
-  constexpr int NW = kWideNW, MB = kWideMB, KSUB = kWideKSub, PD = kRingPD, R = kRingDepth;
+  constexpr int NW = kWideNW, MB = kWideMB, KSUB = kWideKSub, PD = ring_pd(NB), R = kRingDepth;
   constexpr int BN = 16 * NB, NT = 64 * NW, KH = 32 * KSUB, ROW = KH + 16;   // 160-byte rows: conflict-free reads
   constexpr int HP = BN * (KH / 8) / NT;       // 16-byte pieces of H per thread per sub-chunk
   constexpr int NSUB = kKS / KSUB;
