@@ -19,12 +19,14 @@
 // best (measured: 86% of peak, against 75% for 16-row interleaved reads).
 //
 // Four kernels read it:
-//  * GEMV (B <= 2): each lane accumulates bf16 dot products of its row piece
-//    with H (staged once in LDS; the four lanes of a row share nothing but
-//    the reduction), then two butterfly steps finish each row's sum;
+//  * GEMV (B <= 2, when asked for: the MFMA kernel streams this layout
+//    faster): each lane accumulates bf16 dot products of its row piece with
+//    H (staged once in LDS; the four lanes of a row share nothing but the
+//    reduction), then two butterfly steps finish each row's sum;
 //  * MFMA (B up to 64): the A operand comes straight from the loads; H
 //    chunks are staged in LDS and shared by the workgroup's waves, one row
-//    block per wave;
+//    block per wave; a nearly empty last round of tiles runs as half-width
+//    batch tiles in a second launch;
 //  * wide MFMA (B 65 .. 128, and above when D is not a multiple of 256): two
 //    row blocks per wave and 128-column batch tiles, H staged in sub-chunks
 //    and the B operands read one K step ahead;
