@@ -142,7 +142,16 @@ __global__ __launch_bounds__(kThreads) void stage1_gemv_kernel(Stage1Args a) {
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;
 
-    for (int j0 = 0; j0 < nj; j0 += JB) {
+    // With a power-of-two row stride the rows read at one column offset sit
+    // on few memory channels; for power-of-two widths successive row groups
+    // therefore take the row's column blocks in rotated order (measured,
+    // 4096-wide head: 1.7-2.4% faster at B = 1 and 2; no gain at other
+    // widths). Keyed on D, not on the stride, so a padded W sums in the same
+    // order as a contiguous one.
+    const int nblk = (nj + JB - 1) / JB;
+    const int rot = (a.D & (a.D - 1)) == 0 ? (row0 / kRows) % nblk : 0;
+    for (int it = 0; it < nblk; ++it) {
+      const int j0 = (it + rot < nblk ? it + rot : it + rot - nblk) * JB;
       uint4 w[JB][kRows];
 #pragma unroll
       for (int jj = 0; jj < JB; ++jj) {
