@@ -334,27 +334,31 @@ def traffic_record(kernel: str, workload: str, B: int):
 
 
 def oracle_timings(wl, H, W):
-    """The CPU oracle, end to end (widening, fp64 logits, Philox, Gumbel,
-    top-2), on one decode step of this workload at its smallest and largest
-    batch with the host's BLAS threads, and on one thread at B = 1 for the two
-    smallest heads. Returns a list of dicts."""
+    """The CPU oracle on one decode step of this workload at every B of its
+    sweep with the host's BLAS threads, and on one thread at B = 1 for the two
+    smallest heads: end to end (widening, fp64 logits, Philox, Gumbel, top-2),
+    then the fp64 logits alone, so each entry also splits the step into the
+    logits (BLAS) and the rest (noise and argmax, numpy). Returns a list of
+    dicts."""
     import oracle
     from threadpoolctl import threadpool_limits
-    cases = sorted({(min(wl.batches), 0), (max(wl.batches), 0)})
+    cases = [(B, 0) for B in wl.batches]
     if wl.name in ("tiny_f32", "llama3_8b"):
         cases.append((1, 1))
     out = []
     for B, threads in cases:
-        t0 = time.perf_counter()
-        if threads:
-            with threadpool_limits(limits=threads):
-                oracle.sample(H[:B], W, wl.temperature, wl.seed, 0)
-        else:
+        with threadpool_limits(limits=threads if threads else None):
+            t0 = time.perf_counter()
             oracle.sample(H[:B], W, wl.temperature, wl.seed, 0)
-        sec = time.perf_counter() - t0
+            sec = time.perf_counter() - t0
+            t1 = time.perf_counter()
+            oracle.exact_logits(H[:B], W)
+            gemm = time.perf_counter() - t1
         out.append({"workload": wl.name, "B": B, "seconds": round(sec, 3), "samples_per_s": round(B / sec, 2),
+                    "logits_seconds": round(gemm, 3), "noise_and_argmax_seconds": round(max(sec - gemm, 0.0), 3),
                     "threads": threads or "blas default"})
-        log(f"[bench] oracle {wl.name} B={B} ({out[-1]['threads']} threads): {sec:.2f} s")
+        log(f"[bench] oracle {wl.name} B={B} ({out[-1]['threads']} threads): {sec:.2f} s "
+            f"(logits {gemm:.2f} s)")
     return out
 
 
