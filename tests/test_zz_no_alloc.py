@@ -56,6 +56,19 @@ def test_noalloc_equals_workspace_call_twice_then_smaller(fs, kw):
             check_parity(H, W, T, seed, step, np.arange(H.shape[0]), got)
 
 
+@pytest.mark.parametrize("single_pass", [False, True])
+def test_noalloc_split_last_round(fs, single_pass):
+    """A vocabulary whose nearly empty last round of 128-row tiles runs as a
+    second launch of half-width batch tiles: the same tokens as the call with
+    a workspace."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H, W = _head(6, 64, 256, (2 * cus + cus // 5) * 128 + 9)
+    for step in range(2):
+        want, got = _pair(fs, H, W, True, 1.0, 4, step, single_pass=single_pass)
+        assert np.array_equal(got, want)
+
+
 def test_noalloc_single_pass_after_a_dirty_two_stage_call(fs):
     H, W = _head(3, 40, 512, 5003)
     Hd, Wd = to_device(H), to_device(W)
