@@ -71,6 +71,7 @@ struct Plan {
   bool tiled = false;     // W in the tiled layout
   bool single_pass = false;
   int32_t group_size = 0; // > 0: grouped variant
+  int64_t half_tiles = 0; // the last half_tiles of the n_tiles vocab tiles hold 64 rows each
 };
 
 struct FusedCall {
@@ -195,6 +196,23 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   return true;
 }
 
+// The fused call's plan: make_plan's, with the 128-row tiles of a ragged last
+// round of workgroups split into 64-row tiles where the sampling-only tiled
+// kernel runs (one batch tile, no logits store, no log-masses). The count
+// depends on the current device (resident workgroups), so the sizing queries
+// and the call agree on one device.
+bool make_fused_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_options_t* o, Plan* p,
+                     fs_status_t* why) {
+  if (!make_plan(B, D, V, dtype, o, p, why)) return false;
+  if (p->tiled && p->variant == FS_VARIANT_MFMA && p->tile == kTiledMfmaTile && p->group_size == 0 &&
+      !(o && o->logits)) {
+    p->half_tiles = tiled_half_tiles(p->n_tiles, B, p->batch_tile);
+    p->n_tiles += p->half_tiles / 2;
+    if (p->n_tiles > 0x7FFFFFFF) return false;
+  }
+  return true;
+}
+
 hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, hipStream_t stream) {
   if (p.tiled) return launch_stage1_tiled(a, p.variant == FS_VARIANT_MFMA, stream);
   if (p.variant != FS_VARIANT_MFMA) return launch_stage1_gemv(a, dtype, stream);
@@ -263,6 +281,7 @@ Stage1Args stage1_args(const void* H, int64_t ldh, const void* W, int64_t ldw, i
   a.vocab_tile = p.tile;
   a.n_tiles = (int32_t)p.n_tiles;
   a.batch_tile = p.batch_tile;
+  a.half_tiles = (int32_t)p.half_tiles;
   return a;
 }
 
@@ -274,7 +293,7 @@ fs_status_t prepare_fused(const void* H, int64_t ldh, const void* W, int64_t ldw
   fs_status_t st = check_common(H, ldh, W, ldw, dtype, B, D, V, temperature, workspace, out_tokens, opts);
   if (st != FS_OK) return st;
   Plan& p = call->plan;
-  if (!make_plan(B, D, V, dtype, opts, &p, &st)) return st;
+  if (!make_fused_plan(B, D, V, dtype, opts, &p, &st)) return st;
   if (opts && opts->logits) {
     if (!dtype_ok(opts->logits_dtype)) return FS_ERR_UNSUPPORTED;
     if (opts->ld_logits < V) return FS_ERR_INVALID_ARGUMENT;
@@ -382,7 +401,7 @@ int64_t fs_num_vocab_tiles(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, co
   if (!sizes_ok(B, D, V) || !dtype_ok(dtype)) return -1;
   Plan p;
   fs_status_t why;
-  if (!make_plan(B, D, V, dtype, opts, &p, &why)) return -1;
+  if (!make_fused_plan(B, D, V, dtype, opts, &p, &why)) return -1;
   return p.n_tiles;
 }
 
@@ -390,7 +409,7 @@ size_t fs_workspace_bytes_ex(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, 
   if (!sizes_ok(B, D, V) || !dtype_ok(dtype)) return 0;
   Plan p;
   fs_status_t why;
-  if (!make_plan(B, D, V, dtype, opts, &p, &why)) return 0;
+  if (!make_fused_plan(B, D, V, dtype, opts, &p, &why)) return 0;
   return fused_ws_bytes(B, p);
 }
 

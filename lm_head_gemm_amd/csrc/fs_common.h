@@ -257,7 +257,7 @@ struct Stage1Args {
   uint64_t* keys;       // [B] running maximum keys, zero between calls
   uint32_t* counter;    // finished-workgroup counters (kSpGroups + 1 slots), zero between calls
   int32_t* out;         // [B] tokens
-  int32_t split_tiles;  // the last split_tiles vocab tiles run as two half batch tiles (set by the launcher)
+  int32_t half_tiles;   // the last half_tiles vocab tiles hold half a vocab tile of rows each (from the plan)
 };
 
 // Stores l[0..3], the logits of batch row b at vocab rows v0 .. v0+3 (those
@@ -313,15 +313,6 @@ __device__ __forceinline__ bool tile_of(int L, int n_vt, int n_bt, int* vt, int*
   return true;
 }
 
-// Launch index i (counted from the first split slot) -> (vocab tile, batch
-// half) of the split tiles: the two halves of a tile are kXcds slots apart,
-// so they run on one XCD. Returns false for padding slots.
-__device__ __forceinline__ bool split_tile_of(int i, int n_split, int* vt, int* half) {
-  *vt = i / (2 * kXcds) * kXcds + i % kXcds;
-  *half = (i / kXcds) & 1;
-  return *vt < n_split;
-}
-
 // Single-pass bookkeeping in the workspace after the [B] keys: one counter
 // per group of vocab tiles (tile mod kSpGroups) and one for the groups, each
 // in its own 256-byte slot (uint32 index kSpSlot * slot).
@@ -365,14 +356,10 @@ __device__ __forceinline__ void publish_candidates(const Stage1Args& a, int tile
   __builtin_amdgcn_s_waitcnt(0);  // the maxima have been performed
   __syncthreads();
   if (tid == 0) {
-    // workgroups per group: the group's vocab tiles times the batch tiles,
-    // its split tiles (the last a.split_tiles, one batch tile) counted twice
+    // workgroups per group: the group's vocab tiles times the batch tiles
     const int g = tile % kSpGroups;
-    const int whole = a.n_tiles - a.split_tiles;
-    const int n_bt = a.split_tiles ? 1 : a.total_wgs / a.n_tiles;
-    const int tiles = (a.n_tiles - g + kSpGroups - 1) / kSpGroups;
-    const int whole_tiles = whole > g ? (whole - g + kSpGroups - 1) / kSpGroups : 0;
-    const uint32_t in_group = (uint32_t)(whole_tiles * n_bt + 2 * (tiles - whole_tiles));
+    const int n_bt = a.total_wgs / a.n_tiles;
+    const uint32_t in_group = (uint32_t)(((a.n_tiles - g + kSpGroups - 1) / kSpGroups) * n_bt);
     const uint32_t groups = (uint32_t)min(a.n_tiles, kSpGroups);
     int last = 0;
     if (__hip_atomic_fetch_add(a.counter + kSpSlot * g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -398,6 +385,9 @@ hipError_t launch_stage1_gemv(const Stage1Args& a, fs_dtype_t dtype, hipStream_t
 int gemv_batch_tile(int64_t B, int64_t D, fs_dtype_t dtype);
 hipError_t launch_stage1_mfma(const Stage1Args& a, hipStream_t stream);
 hipError_t launch_stage1_tiled(const Stage1Args& a, bool mfma, hipStream_t stream);
+// Sampling on tiled W with n_tiles 128-row vocab tiles: how many 64-row tiles
+// the last round of workgroups becomes (0: none), for the current device.
+int64_t tiled_half_tiles(int64_t n_tiles, int64_t B, int32_t batch_tile);
 bool rows_direct_ok(int64_t D);
 hipError_t launch_stage1_rows_direct(const Stage1Args& a, hipStream_t stream);
 hipError_t launch_stage1_mfma_f32(const Stage1Args& a, hipStream_t stream);

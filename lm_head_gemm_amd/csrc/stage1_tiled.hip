@@ -289,16 +289,27 @@ __device__ __forceinline__ void store_logits_staged(const Stage1Args& a, float* 
   __syncthreads();
 }
 
+// Column blocks whose sums wave half kh (0 or 1) of a 64-row tile finishes:
+// the first half of the blocks for kh = 0, the rest for kh = 1.
+template <int NB>
+__device__ __forceinline__ bool half_owns(int nb, int kh) {
+  return NB == 1 ? kh == 0 : (nb < NB / 2) == (kh == 0);
+}
+
 // Epilogue of the kernels in which each wave owns one 16-row block of a
 // 16 NW-row vocab tile and the workgroup one 16 NB-column batch tile: the
 // optional logits store (staged through `stage`, STAGE_BYTES of LDS the
 // main loop no longer needs), then per batch row the tile's maximiser as one
 // key (and the tile's log-mass with MASS), published for Stage 2 or the
-// single-pass reduction.
-template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS, int STAGE_BYTES>
+// single-pass reduction. With HALF the tile is a 64-row one (tile index vt,
+// first row block rb0): waves w and w + 4 hold row block rb0 + w mod 4, and
+// wave half kh scores only the column blocks half_owns gives it.
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS, int STAGE_BYTES, bool HALF = false>
 __device__ __forceinline__ void narrow_epilogue(const Stage1Args& a, const f32x4 (&acc)[NB], int vt, int b0,
                                                 float* stage, uint64_t (&red)[NW][16 * NB],
-                                                float2 (&red_mass)[MASS ? NW : 1][MASS ? 16 * NB : 1]) {
+                                                float2 (&red_mass)[MASS ? NW : 1][MASS ? 16 * NB : 1],
+                                                int rb0 = 0, int kh = 0) {
+  static_assert(!HALF || (NW == 8 && SAMPLE && !STORE && !MASS), "64-row tiles only sample");
   constexpr int BN = 16 * NB;
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
@@ -306,7 +317,7 @@ __device__ __forceinline__ void narrow_epilogue(const Stage1Args& a, const f32x4
   const int wave = tid >> 6;
   const int r = lane & 15;
   const int q = lane >> 4;
-  const int m = vt * NW + wave;
+  const int m = HALF ? rb0 + (wave & 3) : vt * NW + wave;
   const int v0 = 16 * m + 4 * q;   // this lane's four consecutive vocab rows
   if constexpr (STORE) {
     constexpr int NBC = NB < 2 ? NB : 2;   // 16-column blocks per staging pass
@@ -330,6 +341,10 @@ __device__ __forceinline__ void narrow_epilogue(const Stage1Args& a, const f32x4
       constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
+        if (HALF && !half_owns<NB>(nb, kh)) {
+          if (q == 0) red[wave][nb * 16 + r] = 0ull;   // the other wave half's
+          continue;
+        }
         const int b = b0 + nb * 16 + r;
         uint4 words = make_uint4(0u, 0u, 0u, 0u);
         if constexpr (!kGreedy) words = philox_quad(a.nk, (uint32_t)(v0 >> 2), (uint32_t)b);
@@ -356,7 +371,7 @@ __device__ __forceinline__ void narrow_epilogue(const Stage1Args& a, const f32x4
         }
       }
     };
-    const bool full = (int64_t)(vt + 1) * NW * 16 <= a.V;
+    const bool full = HALF ? (int64_t)(rb0 + 4) * 16 <= a.V : (int64_t)(vt + 1) * NW * 16 <= a.V;
     if (a.greedy) {
       if (full) tile_max(std::true_type{}, std::true_type{});
       else tile_max(std::true_type{}, std::false_type{});
@@ -385,17 +400,17 @@ __device__ __forceinline__ uint4 lane_gather(const uint4& v, int addr) {
                     (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v.w));
 }
 
-// With SPLIT, a launch covers only the last a.split_tiles vocab tiles, each
-// as two workgroups (one per 16 NB-column half of a batch tile twice as wide,
-// n_bt unused); the launch of the other tiles is the one without SPLIT. Where
-// the last round of workgroups would be at most a quarter full, twice as many
-// workgroups with half the matrix and epilogue work each finish it sooner
-// (measured on 4096-wide heads at B = 24 and 64: 12% faster with the last
-// round 6-20% full, slower from about a third). The two halves of a tile read
-// the same W with cached loads and run on one XCD, so the second read is
-// mostly served by its L2; whole tiles stream W past it.
-template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false, bool SPLIT = false>
-__global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32_t n_bt) {
+template <int NB>
+__device__ __forceinline__ void tiled_half_tile(const Stage1Args& a, int vt, int rb0, uint4* lds_h4,
+                                                uint64_t (&red)[8][16 * NB], float2 (&red_mass)[1][1]);
+
+// With HALF (sampling, one batch tile of 32 or 64 columns), the last
+// a.half_tiles vocab tiles hold 64 rows each (tiled_half_tile); the others
+// are the kernel's own. That variant is held to 128 registers (four waves per
+// SIMD, two workgroups per CU), the occupancy of the variant without.
+template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS = false, bool HALF = false>
+__global__ __launch_bounds__(64 * NW, HALF ? 4 : 1) void mfma_tiled_kernel(Stage1Args a,
+                                                                                             int32_t n_bt) {
   constexpr int BN = 16 * NB;
   constexpr int NT = 64 * NW;
   constexpr int HP = BN * (kBK / 8) / NT;   // 16-byte pieces of H per thread per block
@@ -407,11 +422,14 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
 
   int vt, bt;
-  if constexpr (SPLIT) {
-    if (!split_tile_of(blockIdx.x, a.split_tiles, &vt, &bt)) return;  // whole workgroup
-    vt += a.n_tiles - a.split_tiles;
-  } else if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) {
-    return;  // whole workgroup
+  if (!tile_of(blockIdx.x, a.n_tiles, n_bt, &vt, &bt)) return;  // whole workgroup
+  if constexpr (HALF) {
+    static_assert(NW == 8 && NB >= 2 && SAMPLE && !STORE && !MASS, "64-row tiles: sampling, 32-64 columns");
+    const int whole = a.n_tiles - a.half_tiles;
+    if (vt >= whole) {
+      tiled_half_tile<NB>(a, vt, 8 * whole + 4 * (vt - whole), lds_h4, red, red_mass);
+      return;
+    }
   }
 
   const int tid = threadIdx.x;
@@ -429,7 +447,7 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
   constexpr int kTStride = 64;
   const uint4* wt = static_cast<const uint4*>(a.W) + lane;
   auto wblock = [&](int c) { return wt + block_piece(mc, c, nC); };
-  auto wload = [&](const uint4* p) { return SPLIT ? *p : load_stream16(p); };   // else read once: non-temporal
+  auto wload = [&](const uint4* p) { return load_stream16(p); };   // read once: non-temporal
   const uint16_t* H = static_cast<const uint16_t*>(a.H);
 
   // This thread's share of each H block: rows hn[i], columns hk[i] .. +8;
@@ -515,6 +533,146 @@ __global__ __launch_bounds__(64 * NW) void mfma_tiled_kernel(Stage1Args a, int32
 
   narrow_epilogue<NB, NW, SAMPLE, STORE, MASS, (int)sizeof(lds_h4)>(a, acc, vt, b0, reinterpret_cast<float*>(lds_h4),
                                                                      red, red_mass);
+}
+
+// A 64-row vocab tile of the sampling kernel (tile index vt, row blocks
+// rb0 .. rb0 + 3, one batch tile of 16 NB columns), for the tiles of a last
+// round of workgroups that would leave most of the chip idle. Waves w and
+// w + 4 hold row block rb0 + w mod 4 and split each K block between them
+// (K steps 0-3 and 4-7): the workgroup does half of a 128-row tile's matrix
+// work and reads half of its W, none of it twice. H is staged as in the
+// 128-row tile. The two partial sums of a row block meet in LDS, each wave
+// half finishing half of the column blocks; a logit is the sum of its two
+// halves, within fp32 rounding of the 128-row tile's.
+template <int NB>
+__device__ __forceinline__ void tiled_half_tile(const Stage1Args& a, int vt, int rb0, uint4* lds_h4,
+                                                uint64_t (&red)[8][16 * NB], float2 (&red_mass)[1][1]) {
+  constexpr int NW = 8;
+  constexpr int BN = 16 * NB;
+  constexpr int NT = 64 * NW;
+  constexpr int HP = BN * (kBK / 8) / NT;
+  constexpr int KH = kKS / 2;        // K steps of a block per wave half
+  constexpr int kTStride = 64;
+  static_assert(4 * NB * 64 * 16 <= 2 * BN * kLdsRow * 2, "partial sums fit the H buffers");
+  uint16_t* lds_h = reinterpret_cast<uint16_t*>(lds_h4);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int kh = wave >> 2;
+  const int D = a.D;
+  const int nC = (D + kBK - 1) / kBK;
+  const int nM = (a.V + 15) / 16;
+  const int mc = min(rb0 + (wave & 3), nM - 1);
+  const uint4* wt = static_cast<const uint4*>(a.W) + lane + KH * kh * kTStride;
+  auto wblock = [&](int c) { return wt + block_piece(mc, c, nC); };
+  const uint16_t* H = static_cast<const uint16_t*>(a.H);
+
+  int hn[HP], hk[HP];
+#pragma unroll
+  for (int i = 0; i < HP; ++i) {
+    const int p = tid + NT * i;
+    hn[i] = p / (kBK / 8);
+    hk[i] = 8 * (p % (kBK / 8));
+  }
+  auto load_h = [&](int c, uint4 (&h)[HP]) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      const int k = c * kBK + hk[i];
+      h[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (hn[i] < a.B && k < D) h[i] = *reinterpret_cast<const uint4*>(H + (int64_t)hn[i] * a.ldh + k);
+    }
+  };
+  auto store_h = [&](int buf, const uint4 (&h)[HP]) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i)
+      *reinterpret_cast<uint4*>(lds_h + buf * BN * kLdsRow + hn[i] * kLdsRow + hk[i]) = h[i];
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // W two K blocks ahead (register set c mod 2 holds block c, reloaded with
+  // block c + 2 as its matrix instructions issue), so that up to 8 KiB per
+  // wave are in flight as in the 128-row tile, in as many registers.
+  constexpr int KD = 2;
+  uint4 w[KD][KH];
+  uint4 hreg[HP];
+#pragma unroll
+  for (int s = 0; s < KD; ++s) {
+    const uint4* p = wblock(s < nC ? s : 0);
+#pragma unroll
+    for (int t = 0; t < KH; ++t)
+      if (s < nC) w[s][t] = load_stream16(p + t * kTStride);
+  }
+  load_h(0, hreg);
+  store_h(0, hreg);
+  __syncthreads();
+  // Block c's math from register set S; with MORE, block c+1's H is staged on
+  // the way, with AHEAD block c+KD's W is loaded. Both are compile-time in
+  // every call, so the compiler can count the loads in flight (a load under
+  // a run-time condition makes it wait for all of them at each barrier).
+  auto step = [&](int c, auto set_c, auto more_c, auto ahead_c) {
+    constexpr int S = decltype(set_c)::value;
+    constexpr bool kMore = decltype(more_c)::value;
+    constexpr bool kAhead = decltype(ahead_c)::value;
+    if (kMore) load_h(c + 1, hreg);
+    const uint4* p = wblock(kAhead ? c + KD : c);
+    const uint16_t* hb = lds_h + (c & 1) * BN * kLdsRow + 32 * KH * kh + 8 * q;
+#pragma unroll
+    for (int t = 0; t < KH; ++t) {
+      const uint4 x = w[S][t];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint4 bfrag = *reinterpret_cast<const uint4*>(hb + (nb * 16 + r) * kLdsRow + 32 * t);
+        acc[nb] = mfma16x16x32(x, bfrag, acc[nb]);
+      }
+      // the reload stays behind its register's matrix instructions (only ALU
+      // and LDS instructions cross), so it can take the same registers
+      // instead of being copied into them at the loop's back edge
+      if (kAhead) {
+        __builtin_amdgcn_sched_barrier(0x786);
+        w[S][t] = load_stream16(p + t * kTStride);
+      }
+    }
+    if (kMore) {
+      store_h((c + 1) & 1, hreg);
+      __syncthreads();
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Y = std::true_type;
+  using N = std::false_type;
+  int c = 0;
+  for (; c + 3 < nC; c += 2) {
+    step(c, S0{}, Y{}, Y{});
+    step(c + 1, S1{}, Y{}, Y{});
+  }
+  // the last one to three blocks
+  if (c + 2 < nC) {
+    step(c, S0{}, Y{}, Y{});
+    step(c + 1, S1{}, Y{}, N{});
+    step(c + 2, S0{}, N{}, N{});
+  } else if (c + 1 < nC) {
+    step(c, S0{}, Y{}, N{});
+    step(c + 1, S1{}, N{}, N{});
+  } else {
+    step(c, S0{}, N{}, N{});
+  }
+
+  // each wave hands the column blocks it does not finish to its partner
+  __syncthreads();   // every wave is done with H
+  f32x4* X = reinterpret_cast<f32x4*>(lds_h4);   // [row block][column block][lane]
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    if (!half_owns<NB>(nb, kh)) X[((wave & 3) * NB + nb) * 64 + lane] = acc[nb];
+  __syncthreads();
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    if (half_owns<NB>(nb, kh)) acc[nb] += X[((wave & 3) * NB + nb) * 64 + lane];
+  narrow_epilogue<NB, NW, true, false, false, 0, true>(a, acc, vt, 0, nullptr, red, red_mass, rb0, kh);
 }
 
 // ------------------------------------------------------- MFMA, row-major W
@@ -1584,39 +1742,32 @@ int resident_wgs(int threads) {
   return n;
 }
 
-// Vocab tiles to split in two (see mfma_tiled_kernel): those of a last round
-// that would be at most a quarter full, when a full round comes before it.
-int64_t ragged_split(int64_t n_tiles, int64_t slots) {
+// Vocab tiles of the last round of workgroups, when a full round comes
+// before it and the last round is at most a quarter full.
+int64_t ragged_last_round(int64_t n_tiles, int64_t slots) {
   if (slots <= 0 || n_tiles <= slots) return 0;
   const int64_t rem = n_tiles % slots;
   return 4 * rem <= slots ? rem : 0;
 }
 
-// The whole tiles, then (when the last round is split) the split tiles as
-// half-width batch tiles in a second launch on the same stream.
 template <int NB, int NW, bool SAMPLE, bool STORE, bool MASS>
 hipError_t launch_mfma_nb_k(const Stage1Args& a, hipStream_t stream) {
   constexpr int BN = 16 * NB;
-  constexpr auto k = mfma_tiled_kernel<NB, NW, SAMPLE, STORE, MASS>;
   const int n_bt = (a.B + BN - 1) / BN;
-  Stage1Args b = a;
-  b.split_tiles = 0;
-  // both halves of a split tile hold batch rows
-  if (NB % 2 == 0 && n_bt == 1 && a.B > BN / 2)
-    b.split_tiles = (int32_t)ragged_split(a.n_tiles, resident_wgs<k>(64 * NW));
-  const int64_t G = (int64_t)(a.n_tiles - b.split_tiles) * n_bt;
+  const int64_t G = (int64_t)a.n_tiles * n_bt;
   const int64_t grid = n_bt == 1 ? G : (G + kXcds - 1) / kXcds * kXcds;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;   // launch() checks grid x threads
-  b.total_wgs = (int32_t)(G + 2 * (int64_t)b.split_tiles);
-  hipError_t e = launch(k, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b, (int32_t)n_bt);
-  if constexpr (NB % 2 == 0) {
-    if (e == hipSuccess && b.split_tiles > 0) {
-      const int64_t halves = (2 * (int64_t)b.split_tiles + 2 * kXcds - 1) / (2 * kXcds) * (2 * kXcds);
-      e = launch(mfma_tiled_kernel<NB / 2, NW, SAMPLE, STORE, MASS, true>, dim3((unsigned)halves), dim3(64 * NW), 0,
-                 stream, b, (int32_t)1);
-    }
+  Stage1Args b = a;
+  b.total_wgs = (int32_t)G;
+  if (a.half_tiles == 0)
+    return launch(mfma_tiled_kernel<NB, NW, SAMPLE, STORE, MASS>, dim3((unsigned)grid), dim3(64 * NW), 0, stream, b,
+                  (int32_t)n_bt);
+  if constexpr (NW == 8 && NB >= 2 && SAMPLE && !STORE && !MASS) {
+    if (n_bt == 1 && a.half_tiles <= a.n_tiles)
+      return launch(mfma_tiled_kernel<NB, NW, true, false, false, true>, dim3((unsigned)grid), dim3(64 * NW), 0,
+                    stream, b, (int32_t)1);
   }
-  return e;
+  return hipErrorInvalidValue;   // 64-row tiles are planned only for this case
 }
 
 template <int NB, int NW>
@@ -1688,6 +1839,15 @@ int device_cu_count() {
   if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
     cache[dev].store(n, std::memory_order_relaxed);
   return n > 0 ? n : 0;
+}
+
+// Only where the kernel with the 64-row tiles keeps as many workgroups
+// resident as the one without.
+template <int NB>
+int64_t half_tiles_nb(int64_t n_tiles) {
+  const int slots = resident_wgs<mfma_tiled_kernel<NB, 8, true, false, false, true>>(64 * 8);
+  if (slots != resident_wgs<mfma_tiled_kernel<NB, 8, true, false, false>>(64 * 8)) return 0;
+  return 2 * ragged_last_round(n_tiles, slots);
 }
 
 // One 256-column batch tile (one workgroup per CU) when it covers B and the
@@ -1817,6 +1977,23 @@ hipError_t launch_stage1_tiled(const Stage1Args& a, bool mfma, hipStream_t strea
   const bool eight = a.vocab_tile == 128;
   if (mfma) return eight ? launch_mfma_nw<8>(a, stream) : launch_mfma_nw<4>(a, stream);
   return eight ? launch_gemv_nw<8>(a, stream) : launch_gemv_nw<4>(a, stream);
+}
+
+// Sampling with 128-row tiles and one batch tile of 32 or 64 columns: the
+// tiles of a last round of workgroups at most a quarter full run as two
+// 64-row tiles each, in the same launch. Measured on 4096-wide heads with
+// V = 69376, 72064, 78592 and 202048 (last round 6-20% full): 2-4% faster at
+// B = 24 and 1-2% at B = 64 than the same tiles split by batch columns in a
+// second launch, which in turn was 2-7% faster than no split. Not for a last
+// round a third full (the 3584 x 152064 head: 3% slower) nor for 16-column
+// batch tiles (2% slower at 16% full): a lone 128-row tile per CU already
+// keeps more W in flight than its two halves do. Returns the number of
+// 64-row tiles (twice the tiles so split).
+int64_t tiled_half_tiles(int64_t n_tiles, int64_t B, int32_t batch_tile) {
+  const int64_t bn = batch_tile ? batch_tile : (B <= 16 ? 16 : B <= 32 ? 32 : 64);
+  if (B > bn || bn == 16) return 0;
+  if (bn == 32) return half_tiles_nb<2>(n_tiles);
+  return half_tiles_nb<4>(n_tiles);
 }
 
 }  // namespace fs
