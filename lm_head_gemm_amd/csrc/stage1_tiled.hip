@@ -25,8 +25,8 @@
 //    reduction), then two butterfly steps finish each row's sum;
 //  * MFMA (B up to 64): the A operand comes straight from the loads; H
 //    chunks are staged in LDS and shared by the workgroup's waves, one row
-//    block per wave; a nearly empty last round of tiles runs as half-width
-//    batch tiles in a second launch;
+//    block per wave; the tiles of a nearly empty last round run as 64-row
+//    tiles whose two wave halves split the K loop;
 //  * wide MFMA (B 65 .. 128, and above when D is not a multiple of 256): two
 //    row blocks per wave and 128-column batch tiles, H staged in sub-chunks
 //    and the B operands read one K step ahead;

@@ -622,8 +622,8 @@ def test_graph_capture_and_replay(fs, single_pass, B, D, V):
 
 @pytest.mark.parametrize("single_pass", [False, True])
 def test_graph_capture_split_last_round(fs, single_pass):
-    """The same with a nearly empty last round of 128-row tiles, which the
-    launcher runs as a second launch of half-width batch tiles."""
+    """The same with a nearly empty last round of 128-row tiles, which runs
+    as 64-row tiles (the plan's extra candidate slots included)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     _graph_capture_check(fs, single_pass, 64, 256, (2 * cus + cus // 5) * 128 + 9)

@@ -58,9 +58,9 @@ def test_noalloc_equals_workspace_call_twice_then_smaller(fs, kw):
 
 @pytest.mark.parametrize("single_pass", [False, True])
 def test_noalloc_split_last_round(fs, single_pass):
-    """A vocabulary whose nearly empty last round of 128-row tiles runs as a
-    second launch of half-width batch tiles: the same tokens as the call with
-    a workspace."""
+    """A vocabulary whose nearly empty last round of 128-row tiles runs as
+    64-row tiles (more candidate slots in the scratch array): the same tokens
+    as the call with a workspace."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     H, W = _head(6, 64, 256, (2 * cus + cus // 5) * 128 + 9)
