@@ -154,7 +154,12 @@ int fs_last_hip_error(void);
 /* Number of Stage-1 vocab tiles the fused call uses for these sizes (the
  * candidate buffer is [n_tiles, B] 64-bit keys at the start of the
  * workspace, tile-major so each Stage-1 workgroup writes one contiguous
- * run). Returns -1 for invalid sizes or options. */
+ * run). On tiled W with 17-64 rows and 128-row tiles, the tiles of a last
+ * round of resident workgroups at most a quarter full count twice (each runs
+ * as two 64-row tiles); that depends on the current device's compute units
+ * and occupancy, so this query, fs_workspace_bytes_ex and the call agree when
+ * made with the same device current (no device: no such split counted).
+ * Returns -1 for invalid sizes or options. */
 int64_t fs_num_vocab_tiles(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
                            const fs_options_t* opts);
 
@@ -166,7 +171,10 @@ int32_t fs_vocab_tile_granule(fs_variant_t variant);
  * log-mass per (row, vocab tile); with single_pass, B keys and the
  * finished-workgroup counters, 8448 bytes).
  * The size arguments come in the order of the sampling calls' own: B, D, V
- * (batch rows, hidden size, vocabulary rows). 0 on invalid sizes or options. */
+ * (batch rows, hidden size, vocabulary rows). Device-dependent like
+ * fs_num_vocab_tiles (query with the call's device current; a too small
+ * workspace is refused with FS_ERR_WORKSPACE_TOO_SMALL before any launch).
+ * 0 on invalid sizes or options. */
 size_t fs_workspace_bytes(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype);
 size_t fs_workspace_bytes_ex(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype,
                              const fs_options_t* opts);
