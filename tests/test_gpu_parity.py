@@ -299,13 +299,15 @@ def test_tiled_ragged_last_round_split(fs):
     """B = 17 .. 64 on vocabularies whose 128-row tiles leave the last round
     of two-per-CU workgroups at most a quarter full (those tiles then run as
     two 64-row tiles each, the plan counting them): one split tile, a last
-    64-row tile with no vocab row, a ragged D, several K blocks. Every row
-    against the oracle, greedy, single-pass, the grouped variant and stored
-    logits (paths without the 64-row tiles)."""
+    64-row tile with no vocab row, a ragged D, 1 to 5 K blocks (each way
+    the loop that keeps W two blocks ahead can end). Every row against the
+    oracle, greedy, single-pass, the grouped variant and stored logits
+    (paths without the 64-row tiles)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for B, D, V in [(64, 256, (2 * cus + cus // 3) * 128 + 5), (40, 512, (4 * cus + 1) * 128),
-                    (24, 264, (2 * cus + cus // 2) * 128 - 3), (17, 1024, (2 * cus + cus // 8) * 128 + 70)]:
+                    (24, 264, (2 * cus + cus // 2) * 128 - 3), (17, 1024, (2 * cus + cus // 8) * 128 + 70),
+                    (33, 768, (2 * cus + cus // 6) * 128 + 17), (48, 1280, (2 * cus + cus // 7) * 128)]:
         assert fs.num_vocab_tiles(B, D, V, tiled=True) > -(-V // 128)   # 64-row tiles planned
         H, W = _rand_head(B + D + V, B, D, V)
         Hd = to_device(H)
