@@ -119,7 +119,8 @@ bool make_plan(int64_t B, int64_t D, int64_t V, fs_dtype_t dtype, const fs_optio
   if (bt == kTiledBigBatch) {
     // the 256 x 256 tile: tiled bf16 W, D a multiple of 32, plain sampling
     const bool ok = layout == FS_LAYOUT_TILED && dtype == FS_DTYPE_BF16 && D % 32 == 0 && group_size == 0 &&
-                    !(o && o->logits) && variant != FS_VARIANT_GEMV && (o->vocab_tile == 0 || o->vocab_tile == kTiledWideTile);
+                    !(o && o->logits) && variant != FS_VARIANT_GEMV &&
+                    (o->vocab_tile == 0 || o->vocab_tile == kTiledWideTile);
     if (!ok) {
       *why = FS_ERR_UNSUPPORTED;
       return false;
@@ -222,7 +223,9 @@ hipError_t launch_stage1(const Plan& p, const Stage1Args& a, fs_dtype_t dtype, h
   return rows_direct_ok(a.D) ? launch_stage1_rows_direct(a, stream) : launch_stage1_mfma(a, stream);
 }
 
-size_t cand_bytes(int64_t B, const Plan& p) { return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign); }
+size_t cand_bytes(int64_t B, const Plan& p) {
+  return align_up((size_t)B * (size_t)p.n_tiles * sizeof(uint64_t), kAlign);
+}
 
 size_t fused_ws_bytes(int64_t B, const Plan& p) {
   if (p.single_pass)   // keys + the counters, one 256-byte slot each

@@ -39,7 +39,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKS = 8;               // MFMA K steps (of 32) per K chunk
 constexpr int kBK = 32 * kKS;        // 256
-constexpr int kLdsRow = kBK + 16;    // padded H row in LDS (elements): a stride of an odd multiple of 32 bytes reads conflict-free
+// padded H row in LDS (elements): a stride of an odd multiple of 32 bytes reads conflict-free
+constexpr int kLdsRow = kBK + 16;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -536,14 +536,14 @@ __global__ __launch_bounds__(64 * NW, HALF ? 4 : 1) void mfma_tiled_kernel(Stage
 }
 
 // A 64-row vocab tile of the sampling kernel (tile index vt, row blocks
-// rb0 .. rb0 + 3, one batch tile of 16 NB columns), for the tiles of a last
-// round of workgroups that would leave most of the chip idle. Waves w and
-// w + 4 hold row block rb0 + w mod 4 and split each K block between them
-// (K steps 0-3 and 4-7): the workgroup does half of a 128-row tile's matrix
-// work and reads half of its W, none of it twice. H is staged as in the
-// 128-row tile. The two partial sums of a row block meet in LDS, each wave
-// half finishing half of the column blocks; a logit is the sum of its two
-// halves, within fp32 rounding of the 128-row tile's.
+// rb0 .. rb0 + 3, one batch tile of 16 NB columns, NB = 2 or 4), for the
+// tiles of a last round of workgroups that would leave most of the chip idle.
+// Waves w and w + 4 hold row block rb0 + w mod 4 and split each K block
+// between them (K steps 0-3 and 4-7): the workgroup does half of a 128-row
+// tile's matrix work and reads half of its W, none of it twice. H is staged
+// as in the 128-row tile. The two partial sums of a row block meet in LDS,
+// each wave half finishing half of the column blocks; a logit is the sum of
+// its two halves, within fp32 rounding of the 128-row tile's.
 template <int NB>
 __device__ __forceinline__ void tiled_half_tile(const Stage1Args& a, int vt, int rb0, uint4* lds_h4,
                                                 uint64_t (&red)[8][16 * NB], float2 (&red_mass)[1][1]) {
