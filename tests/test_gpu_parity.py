@@ -474,6 +474,43 @@ def test_nan_row_returns_minus_one(fs):
         assert r.margin[0] <= TOL or got[2] == r.idx[0]
 
 
+def test_tiled_split_last_round_ties_and_nan_rows(fs):
+    """Exact ties and an all-NaN row where the last round runs as 64-row
+    tiles. Two equal W rows in tiles of one kind (both 128-row, or both
+    64-row, the two halves of one split tile included) get bit-equal logits,
+    so greedy takes the lower index; across the seam between the kinds the
+    sums are taken in another order, so either index is a correct answer
+    (the tie rule for near-ties). Sampled rows against the oracle,
+    single-pass equal to two-stage; the NaN row gives -1."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, D, V = 24, 256, (2 * cus + cus // 8) * 128 + 40
+    n128 = -(-V // 128)
+    split = fs.num_vocab_tiles(B, D, V, tiled=True) - n128
+    assert split > 0
+    first = 128 * (n128 - split)              # first row of the 64-row tiles
+    same = [(3, 700), (first + 63, first + 64), (first + 64 * 3 + 5, first + 64 * 5 + 9)]
+    cross = [(first - 1, first), (0, V - 1)]
+    pairs = same + cross
+    H, W = _rand_head(11, B, D, V)
+    hv = inputs.bf16_bits_to_f32(H)
+    for b, (lo, hi) in enumerate(pairs):
+        W[lo] = inputs.f32_to_bf16_bits(hv[b] * np.float32(0.5))
+        W[hi] = W[lo]
+    nan_row = len(pairs)
+    H[nan_row, :] = inputs.f32_to_bf16_bits(np.full(D, np.nan, dtype=np.float32))
+    Hd, tw = to_device(H), fs.TiledWeights(to_device(W))
+    rows = np.array([b for b in range(B) if b != nan_row])
+    for T in (0.0, 1.0):
+        tok = fs.sample_fused(Hd, tw, T, 3, 1).cpu().numpy()
+        assert tok[nan_row] == -1
+        check_parity(H, W, T, 3, 1, rows, tok[rows])
+        if T == 0.0:
+            for b, (lo, hi) in enumerate(pairs):
+                assert tok[b] == lo if b < len(same) else tok[b] in (lo, hi), (b, tok[b], lo, hi)
+        assert np.array_equal(tok, fs.sample_fused(Hd, tw, T, 3, 1, single_pass=True).cpu().numpy())
+
+
 def test_out_of_range_noise_keys(fs):
     """Large seeds and steps whose high words are non-zero."""
     B, D, V = 4, 128, 2000
